@@ -1,0 +1,195 @@
+"""Pins for the oracle's attention backward against facts fixed outside the oracle:
+hand-worked fixtures, central differences, torch autograd of an independently written
+forward, special cases with closed forms, bilinear identities and structural
+equivalences (GQA = MHA on replicated caches, LSE recompute = saved P = fresh softmax)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import specs, verify
+import synth
+
+
+def _golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "attention_hand.json")))
+    ln3 = math.log(3.0)
+    ev = lambda v: eval(str(v), {"ln3": ln3}) if isinstance(v, str) else v
+    fix = lambda a: np.array([[ev(x) for x in row] if isinstance(row, list) else ev(row) for row in a], dtype=np.float64)
+    return [{k: (fix(v) if isinstance(v, list) else v) for k, v in c.items()} for c in g["cases"]]
+
+
+def test_hand_fixture_single_head_specs(golden_dir):
+    for c in _golden(golden_dir):
+        q, K, V, do, sc = c["q"], c["K"], c["V"], c["dout"], c["scale"]
+        np.testing.assert_allclose(specs.attention_forward(q, K, V, sc), c["out"], atol=1e-15)
+        np.testing.assert_allclose(specs.attention_backward_q(q, K, V, sc, do), c["dq"], atol=1e-15)
+        np.testing.assert_allclose(specs.attention_backward_k(q, K, V, sc, do), c["dK"], atol=1e-15)
+        np.testing.assert_allclose(specs.attention_backward_v(q, K, sc, do), c["dV"], atol=1e-15)
+
+
+def test_hand_fixture_batched(golden_dir):
+    for c in _golden(golden_dir):
+        q = c["q"][None, None, None, :]
+        K, V = c["K"][None, :, None, :], c["V"][None, :, None, :]
+        do = c["dout"][None, None, None, :]
+        dq, dk, dv = A.attention_backward(q, K, V, do, c["scale"], causal=False)
+        np.testing.assert_allclose(dq[0, 0, 0], c["dq"], atol=1e-15)
+        np.testing.assert_allclose(dk[0, :, 0], c["dK"], atol=1e-15)
+        np.testing.assert_allclose(dv[0, :, 0], c["dV"], atol=1e-15)
+
+
+def test_batched_equals_page_single_head_on_tiny_workload():
+    t = synth.tiny_inputs()
+    q, k, v, do = t["q"], t["k"], t["v"], t["dout"]
+    dq, dk, dv = A.attention_backward(q, k, v, do, t["scale"], causal=False)
+    q1, K1, V1, d1 = q[0, 0, 0], k[0, :, 0], v[0, :, 0], do[0, 0, 0]
+    np.testing.assert_allclose(dq[0, 0, 0], specs.attention_backward_q(q1, K1, V1, t["scale"], d1), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[0, :, 0], specs.attention_backward_k(q1, K1, V1, t["scale"], d1), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv[0, :, 0], specs.attention_backward_v(q1, K1, t["scale"], d1), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, Tq=3, Tk=4, Hq=2, Hkv=1, d=4, causal=True),
+    dict(B=2, Tq=4, Tk=4, Hq=2, Hkv=2, d=3, causal=True),
+    dict(B=1, Tq=2, Tk=5, Hq=4, Hkv=2, d=4, causal=False),
+    dict(B=1, Tq=1, Tk=6, Hq=4, Hkv=1, d=4, causal=True),
+])
+def test_attention_fd_page_tolerance(shape):
+    res = verify.verify_attention_backward(**shape, seed=2)
+    assert all(res.values()), res
+
+
+def _torch_attention(q, k, v, scale, causal):
+    """Forward written independently with torch ops ([B,T,H,d] layout)."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    kk = k.repeat_interleave(g, dim=2)
+    vv = v.repeat_interleave(g, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", q, kk) * scale
+    if causal:
+        i = torch.arange(Tq)[:, None]
+        j = torch.arange(Tk)[None, :]
+        s = s.masked_fill(j > i + (Tk - Tq), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    return torch.einsum("bhij,bjhd->bihd", p, vv)
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv,Tq,Tk", [(True, 4, 2, 9, 9), (False, 3, 3, 5, 11), (True, 4, 1, 6, 13)])
+def test_attention_matches_autograd(causal, Hq, Hkv, Tq, Tk):
+    x = synth.attention_inputs(2, Tq, Tk, Hq, Hkv, 8, "f32", seed=21)
+    scale = 0.3
+    ts = {n: torch.tensor(x[n].astype(np.float64), requires_grad=True) for n in ("q", "k", "v")}
+    o = _torch_attention(ts["q"], ts["k"], ts["v"], scale, causal)
+    (o * torch.tensor(x["dout"].astype(np.float64))).sum().backward()
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], scale, causal)
+    for ours, ref in ((dq, ts["q"].grad), (dk, ts["k"].grad), (dv, ts["v"].grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_single_key_reduces_to_copy():
+    # Tk = 1: P = 1, so dS = 0 (dQ = dK = 0) and dV = dO.
+    x = synth.attention_inputs(2, 1, 1, 3, 3, 8, seed=4)
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.5, causal=True)
+    assert np.max(np.abs(dq)) == 0.0 and np.max(np.abs(dk)) == 0.0
+    np.testing.assert_allclose(dv, x["dout"].astype(np.float64), atol=0)
+
+
+def test_equal_keys_give_zero_dq():
+    x = synth.attention_inputs(1, 4, 6, 2, 2, 8, seed=5)
+    k = np.repeat(x["k"][:, :1], 6, axis=1)
+    dq, _, _ = A.attention_backward(x["q"], k, x["v"], x["dout"], 0.7, causal=False)
+    assert np.max(np.abs(dq)) < 1e-14
+
+
+def test_causal_first_row_has_zero_dq():
+    x = synth.attention_inputs(1, 8, 8, 2, 2, 8, seed=6)
+    dq, _, _ = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.4, causal=True)
+    assert np.max(np.abs(dq[:, 0])) == 0.0 and np.max(np.abs(dq[:, 1])) > 0
+
+
+def test_bilinear_identities():
+    # <dQ,Q> = <dK,K> = sum dS o S and <dV,V> = <dO,O>, for GQA and causal too.
+    x = synth.attention_inputs(2, 12, 12, 4, 2, 16, seed=7)
+    sc = 0.25
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True)
+    O, _ = A.attention_forward(x["q"], x["k"], x["v"], sc, causal=True)
+    qd = np.sum(dq * x["q"])
+    kd = np.sum(dk * x["k"])
+    assert qd == pytest.approx(kd, rel=1e-11)
+    assert np.sum(dv * x["v"]) == pytest.approx(np.sum(O * x["dout"]), rel=1e-11)
+
+
+def test_row_dot_equals_do_dot_o():
+    # D_i = rowsum(P o dP) = dO_i . O_i
+    x = synth.attention_inputs(1, 10, 10, 2, 2, 8, seed=8)
+    sc = 0.35
+    O, lse, P = A.attention_forward(x["q"], x["k"], x["v"], sc, causal=True, want_p=True)
+    dP = np.einsum("bihd,bjhd->bhij", x["dout"].astype(np.float64), x["v"].astype(np.float64))
+    D = A.softmax_row_dot(P, dP)
+    np.testing.assert_allclose(D, np.einsum("bihd,bihd->bhi", x["dout"].astype(np.float64), O), rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_equals_mha_on_replicated_caches():
+    x = synth.attention_inputs(2, 7, 9, 6, 2, 8, seed=9)
+    g = 3
+    sc = 0.3
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True)
+    kr, vr = np.repeat(x["k"], g, axis=2), np.repeat(x["v"], g, axis=2)
+    dq2, dk2, dv2 = A.attention_backward(x["q"], kr, vr, x["dout"], sc, causal=True)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dk, dk2.reshape(2, 9, 2, g, 8).sum(3), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(2, 9, 2, g, 8).sum(3), rtol=1e-12, atol=1e-13)
+
+
+def test_lse_recompute_equals_saved_p_equals_fresh_softmax():
+    x = synth.attention_inputs(1, 9, 12, 4, 2, 8, seed=10)
+    sc = 0.3
+    _, lse, P = A.attention_forward(x["q"], x["k"], x["v"], sc, causal=True, want_p=True)
+    r0 = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True)
+    r1 = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, lse=lse)
+    r2 = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, P=P)
+    for a, b, c in zip(r0, r1, r2):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(a, c, rtol=1e-12, atol=1e-14)
+
+
+def test_lse_matches_logsumexp():
+    x = synth.attention_inputs(1, 5, 8, 2, 1, 4, seed=12)
+    sc = 0.9
+    lse = A.attention_lse(x["q"], x["k"], sc, causal=True)
+    q, k = x["q"].astype(np.float64), x["k"].astype(np.float64)
+    for h in range(2):
+        for i in range(5):
+            s = [sc * np.dot(q[0, i, h], k[0, j, 0]) for j in range(i + 3 + 1)]
+            assert lse[0, h, i] == pytest.approx(math.log(sum(math.exp(v) for v in s)), rel=1e-13)
+
+
+def test_row_blocking_changes_nothing():
+    x = synth.attention_inputs(1, 37, 41, 2, 1, 8, seed=13)
+    a = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.3, True, row_block=1024)
+    b = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.3, True, row_block=8)
+    for u, w in zip(a, b):
+        np.testing.assert_allclose(u, w, rtol=1e-13, atol=1e-14)
+
+
+def test_kv_head_subset_matches_full():
+    x = synth.attention_inputs(1, 6, 6, 4, 2, 8, seed=14)
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.3, True)
+    sq, sk, sv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], 0.3, True, kv_heads=[1])
+    np.testing.assert_allclose(sq, dq[:, :, 2:4], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(sk[:, :, 0], dk[:, :, 1], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(sv[:, :, 0], dv[:, :, 1], rtol=1e-13, atol=1e-15)
+
+
+def test_bottom_right_causal_alignment():
+    # With Tq < Tk the last query sees every key; the first sees Tk - Tq + 1 keys.
+    vis = A.visible_keys(3, 7, True)
+    assert vis[2].all() and vis[0].sum() == 5
+    assert np.array_equal(A.visible_keys(4, 4, True), np.tril(np.ones((4, 4), bool)))
