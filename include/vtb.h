@@ -1,0 +1,177 @@
+/*
+ * vtb.h -- C ABI of the MI355X (gfx950) attention-layer backward library (libvtb.so).
+ *
+ * The operations are the vector-Jacobian products stated on the
+ * "Hesper.Training.VerifiedBackward" API page (sections "Softmax", "RoPE (Rotary Position
+ * Embedding)", "RMSNorm", "Scaled Dot-Product", "Attention (full single-head)"), the
+ * linear backward and per-layer reverse chain of the Hesper pull-request commit log,
+ * and the batched causal multi-head form of the DaisyChain-Train transformer.js page
+ * (function `backward`).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never
+ *     allocates, frees or keeps caller memory; scratch space comes in through an
+ *     explicit `workspace` argument sized by the matching *_workspace_size() query.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream). They
+ *     never synchronise; the caller records events or synchronises.
+ *   - Every call returns a vtb_status. Arguments are validated before anything is
+ *     launched, so a call that fails validation has launched nothing. Outputs are
+ *     undefined after any error. vtb_last_error() gives a thread-local detail string.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Accumulation is always fp32, whatever the storage type.
+ *   - Calls are stateless and may run concurrently on different streams, each with its
+ *     own workspace.
+ */
+#ifndef VTB_H
+#define VTB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* vtb_stream_t; /* a hipStream_t */
+
+typedef enum {
+  VTB_OK = 0,
+  VTB_ERR_ARG = 1,          /* bad shape, stride, NULL pointer or value */
+  VTB_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. head_dim 96) */
+  VTB_ERR_ALIAS = 3,        /* an output overlaps an input or another output */
+  VTB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the size query returns */
+  VTB_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} vtb_status;
+
+typedef enum { VTB_F32 = 0, VTB_BF16 = 1 } vtb_dtype;
+
+/* Static name of a status code. */
+const char* vtb_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* vtb_last_error(void);
+/* ABI version: increases when a signature or struct layout changes. */
+int vtb_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Attention backward.
+ *
+ * "Hesper.Training.VerifiedBackward", section "Attention (full single-head)":
+ * attentionBackwardQ (dAttn = dOut . V^T, dScores = softmaxBackward, dQ = scale dScores K)
+ * and attentionBackwardV (dV = attn^T dOut), with scaledDotBackwardK for dK, applied to
+ * every query row of every head:
+ *     P  = exp(scale Q K^T - lse)          (or the saved softmax P when given)
+ *     dP = dO V^T;   D = rowsum(P o dP);   dS = P o (dP - D)
+ *     dQ = scale dS K;   dK = scale dS^T Q;   dV = P^T dO
+ * Causal visibility follows transformer.js (key tj visible to query ti iff tj <= ti),
+ * aligned bottom-right when Tq != Tk: key j is visible to query i iff j <= i + Tk - Tq.
+ * Grouped queries: q-head h reads kv-head h / (Hq / Hkv); dK and dV sum the group's heads.
+ *
+ * Layout: q, dout, dq are [B, Tq, Hq, D]; k, v, dk, dv are [B, Tk, Hkv, D], each with its
+ * own (batch, token, head) strides in ELEMENTS and D contiguous (stride 1).
+ * lse is [B, Hq, Tq] fp32 contiguous: natural-log sum over visible keys of
+ * exp(scale q.k). P is [B, Hq, Tq, Tk] fp32 contiguous; entries at invisible
+ * positions are ignored. D must be 64 or 128.
+ * -------------------------------------------------------------------------------------*/
+typedef struct {
+  int32_t B, Hq, Hkv, Tq, Tk, D;
+  float scale;
+  int32_t causal;      /* 0 or 1; causal requires Tk >= Tq */
+  int32_t in_dtype;    /* vtb_dtype of q, k, v, dout */
+  int32_t out_dtype;   /* vtb_dtype of dq, dk, dv */
+  int64_t s_q[3], s_k[3], s_v[3], s_do[3], s_dq[3], s_dk[3], s_dv[3]; /* (b, t, h) strides */
+} attn_bwd_desc;
+
+/* Bytes of workspace attn_bwd needs for this descriptor (0 on an invalid descriptor). */
+size_t attn_bwd_workspace_size(const attn_bwd_desc* desc);
+
+/* lse: NULL => computed internally from q, k. P: non-NULL => used as the softmax, and
+ * lse is ignored. dq, dk, dv must all be non-NULL and must not overlap each other or any
+ * input. Tk == 0 is an error; Tq == 0 (or B == 0) writes zero dk, dv. */
+int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
+             const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, vtb_stream_t stream);
+
+/* Forward statistics the backward consumes: lse [B, Hq, Tq] fp32 (written), the row
+ * log-sum-exp of the scaled scores over visible keys ("Attention (full single-head)",
+ * attentionForward's softmax normaliser). Uses desc's q/k strides, dtypes and mask. */
+int attn_fwd_lse(const attn_bwd_desc* desc, const void* q, const void* k, float* lse,
+                 vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * RoPE backward: "Hesper.Training.VerifiedBackward", section "RoPE (Rotary Position
+ * Embedding)", ropeBackward = rotation by -theta:
+ *     (dx0, dx1) = (dy0 cos t + dy1 sin t, -dy0 sin t + dy1 cos t)
+ * with theta(pos, i) = pos * base^(-2i / head_dim), i = 0 .. head_dim/2 - 1.
+ * dy, dx: [n_tok, n_heads, head_dim] fp32, token stride tok_stride (elements), heads
+ * packed (head stride = head_dim). pos: device int32 [n_tok] or NULL for pos0 + t.
+ * layout 0 pairs (2i, 2i+1); layout 1 pairs (i, i + head_dim/2). head_dim must be even.
+ * dx == dy (exactly in place) is allowed; any other overlap is VTB_ERR_ALIAS.
+ * -------------------------------------------------------------------------------------*/
+int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim,
+             int64_t tok_stride, const int32_t* pos, int32_t pos0, double base, int32_t layout,
+             vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * RMSNorm backward: "Hesper.Training.VerifiedBackward", section "RMSNorm",
+ * rmsNormBackward, per row of n values:
+ *     rms = sqrt(mean(x^2) + eps);  c = sum_j dy_j gamma_j x_j
+ *     dx_i = (dy_i gamma_i - x_i c / (n rms^2)) / rms
+ * x, dy, dx: [rows, n] fp32 contiguous; gamma: [n] fp32. dx must not overlap inputs.
+ * -------------------------------------------------------------------------------------*/
+int rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int32_t rows,
+                int32_t n, float eps, vtb_stream_t stream);
+
+/* Fused tail of one layer's backward (RoPE backward, RMSNorm backward, residual):
+ *     dh_in = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq))
+ * per token row of C = n_heads * head_dim values, positions pos0 + t. dq: [T, C] fp32
+ * scaled by dq_scale on read; x, dh_out, dh_in: [T, C]; gamma: [C]. dh_in == dh_out is
+ * allowed (in place); other overlaps are VTB_ERR_ALIAS. */
+int rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const float* gamma,
+                         const float* dh_out, float* dh_in, int32_t T, int32_t n_heads,
+                         int32_t head_dim, int32_t pos0, double base, int32_t layout, float eps,
+                         vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Linear backward of Y = X W (Hesper commit log: outer-product dW and transposed dX;
+ * transformer.js `backward`, Wo: gWo = ctxOut^T dx2, dctx = dx2 Wo^T):
+ *     dX = dY W^T   [T, K]        dW = X^T dY = sum_t x_t (outer) dy_t   [K, N]
+ * x: [T, K], w: [K, N], dy: [T, N], all fp32 row-major contiguous. dx or dw may be NULL
+ * (that product is skipped), not both. Outputs must not overlap inputs or each other.
+ * -------------------------------------------------------------------------------------*/
+int linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw, int32_t T,
+               int32_t K, int32_t N, vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * One layer's backward, the Hesper commit log's reverse chain over saved activations
+ * (linear backward, attention backward with the saved softmax, RoPE backward, RMSNorm
+ * backward, residual passing the hidden gradient through unchanged):
+ *     dO, dW   = dh_out W^T,  o^T dh_out
+ *     dq, dK, dV = attention backward (saved P, causal per cfg)
+ *     dh_in    = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq))    (positions 0..T-1)
+ * Saved tensors (fp32): x [T, C] RMSNorm input, gamma [C], w [C, C], o [T, C] attention
+ * output, q [T, H, D] rotated queries, k, v [T, H, D] caches, P [H, T, T] softmax.
+ * Outputs: dh_in [T, C], dw [C, C], dk, dv [T, H, D]. C = H * D; D must be 64 or 128.
+ * dh_in == dh_out is allowed. A 30-layer stack calls this from the last layer down.
+ * -------------------------------------------------------------------------------------*/
+typedef struct {
+  int32_t T, H, D;
+  float scale, eps;
+  double rope_base;
+  int32_t rope_layout, causal;
+} layer_bwd_cfg;
+
+typedef struct {
+  const float *x, *gamma, *w, *o, *q, *k, *v, *P;
+} layer_saved;
+
+size_t layer_bwd_workspace_size(const layer_bwd_cfg* cfg);
+
+int layer_bwd(const layer_bwd_cfg* cfg, const layer_saved* saved, const float* dh_out,
+              float* dh_in, float* dw, float* dk, float* dv, void* workspace,
+              size_t workspace_bytes, vtb_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VTB_H */

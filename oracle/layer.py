@@ -99,10 +99,10 @@ def rmsnorm_backward_rows(x, gamma, dy, eps: float = 1e-6) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- layer
 
-def layer_forward(h, gamma, K, V, W, H: int, scale: float, eps: float = 1e-6,
-                  base: float = 10000.0, causal: bool = True, layout: int = 0):
-    """Forward of one layer (module docstring); returns (out, saved) where saved holds
-    what the backward reads: x (= h), gamma, W, o, q, K, V, P."""
+def layer_saved(h, gamma, K, V, W, H: int, scale: float, eps: float = 1e-6,
+                base: float = 10000.0, causal: bool = True, layout: int = 0):
+    """The tensors one layer's backward reads, from its forward (module docstring):
+    x (= h), gamma, W, o, q, K, V, P."""
     h = _f64(h)
     T, C = h.shape
     d = C // H
@@ -110,18 +110,26 @@ def layer_forward(h, gamma, K, V, W, H: int, scale: float, eps: float = 1e-6,
     q = rope_forward_rows(n.reshape(T, H, d), np.arange(T), base, layout)
     O, _lse, P = attention_forward(q[None], _f64(K)[None], _f64(V)[None], scale, causal, want_p=True)
     o = O[0].reshape(T, C)
-    out = h + linear_forward(o, W)
-    saved = dict(x=h, gamma=_f64(gamma), W=_f64(W), o=o, q=q, K=_f64(K), V=_f64(V), P=P[0])
-    return out, saved
+    return dict(x=h, gamma=_f64(gamma), W=_f64(W), o=o, q=q, K=_f64(K), V=_f64(V), P=P[0])
+
+
+def layer_forward(h, gamma, K, V, W, H: int, scale: float, eps: float = 1e-6,
+                  base: float = 10000.0, causal: bool = True, layout: int = 0):
+    """Forward of one layer (module docstring); returns (out, saved)."""
+    saved = layer_saved(h, gamma, K, V, W, H, scale, eps, base, causal, layout)
+    return saved["x"] + linear_forward(saved["o"], W), saved
 
 
 def layer_backward(saved, g, H: int, scale: float, eps: float = 1e-6,
-                   base: float = 10000.0, causal: bool = True, layout: int = 0):
-    """Backward of one layer: returns (g_in, dW, dK, dV)."""
+                   base: float = 10000.0, causal: bool = True, layout: int = 0, want_dw: bool = True):
+    """Backward of one layer: returns (g_in, dW, dK, dV); dW is None when not wanted."""
     g = _f64(g)
     T, C = g.shape
     d = C // H
-    d_o, dW = linear_backward(saved["o"], saved["W"], g)
+    if want_dw:
+        d_o, dW = linear_backward(saved["o"], saved["W"], g)
+    else:
+        d_o, dW = g @ saved["W"].T, None
     dq, dK, dV = attention_backward(saved["q"][None], saved["K"][None], saved["V"][None],
                                     d_o.reshape(1, T, H, d), scale, causal, P=saved["P"][None])
     dn = rope_backward_rows(dq[0], np.arange(T), base, layout)

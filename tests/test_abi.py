@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/vtb.h
+declares, and rejects bad arguments with the documented status before launching."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import verified_transformer_backward_amd as vtb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "vtb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
+    return sorted(names - {"sizeof", "defined"})
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for n in ("attn_bwd", "rope_bwd", "rmsnorm_bwd", "linear_bwd", "layer_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    L = vtb.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+    assert set(_declared_functions()) == set(vtb.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = vtb.lib()
+    assert L.vtb_status_string(0) == b"VTB_OK"
+    assert L.vtb_status_string(4) == b"VTB_ERR_WORKSPACE"
+    assert L.vtb_abi_version() >= 1
+
+
+# Fake, never-dereferenced device addresses: validation must fail before any launch.
+A0, A1, A2, A3, A4, A5, A6, WS = (0x7F0000000000 + i * 0x10000000 for i in range(8))
+
+
+def _desc(**kw):
+    d = vtb.AttnBwdDesc()
+    B, Tq, Tk, Hq, Hkv, D = kw.get("B", 1), kw.get("Tq", 8), kw.get("Tk", 8), kw.get("Hq", 2), kw.get("Hkv", 2), kw.get("D", 64)
+    d.B, d.Tq, d.Tk, d.Hq, d.Hkv, d.D = B, Tq, Tk, Hq, Hkv, D
+    d.scale, d.causal = kw.get("scale", 0.125), kw.get("causal", 1)
+    d.in_dtype = d.out_dtype = kw.get("dtype", vtb.VTB_F32)
+    for f, H, T in (("s_q", Hq, Tq), ("s_k", Hkv, Tk), ("s_v", Hkv, Tk), ("s_do", Hq, Tq), ("s_dq", Hq, Tq), ("s_dk", Hkv, Tk), ("s_dv", Hkv, Tk)):
+        getattr(d, f)[:] = (T * H * D, H * D, D)
+    return d
+
+
+def _call(d, dq=A4, ws=WS, wsb=1 << 30, lse=None):
+    return vtb.lib().attn_bwd(ctypes.byref(d), A0, A1, A2, A3, lse, None, dq, A5, A6, ws, wsb, None)
+
+
+def test_attn_bwd_validation_codes():
+    L = vtb.lib()
+    assert L.attn_bwd(None, A0, A1, A2, A3, None, None, A4, A5, A6, WS, 1 << 30, None) == 1
+    assert _call(_desc(D=96)) == 2
+    assert _call(_desc(Hq=3, Hkv=2)) == 1
+    assert _call(_desc(Tq=9, Tk=8, causal=1)) == 1
+    assert _call(_desc(Tk=0)) == 1
+    assert _call(_desc(dtype=7)) == 1
+    assert _call(_desc(), dq=A0) == 3                      # dq aliases q
+    assert _call(_desc(), ws=None) == 4
+    assert _call(_desc(), wsb=16) == 4
+    d = _desc()
+    d.s_q[1] = 12                                           # stride not a multiple of 8
+    assert _call(d) == 2
+    assert b"stride" in L.vtb_last_error()
+
+
+def test_attn_workspace_query():
+    assert vtb.attn_bwd_workspace_size(_desc(D=96)) == 0
+    d = _desc(B=4, Tq=512, Tk=512, Hq=20, Hkv=20, D=128, dtype=vtb.VTB_BF16)
+    n = vtb.attn_bwd_workspace_size(d)
+    assert n >= 4 * 512 * 20 * 128 * 4          # fp32 dQ accumulator at least
+
+
+def test_elementwise_and_linear_validation_codes():
+    L = vtb.lib()
+    assert L.rope_bwd(A0, A1, 4, 2, 7, 14, None, 0, 10000.0, 0, None) == 1       # odd head_dim
+    assert L.rope_bwd(A0, A0 + 8, 4, 2, 8, 16, None, 0, 10000.0, 0, None) == 3    # partial overlap
+    assert L.rope_bwd(A0, A1, 4, 2, 8, 16, None, 0, 10000.0, 5, None) == 1        # layout
+    assert L.rmsnorm_bwd(A0, A1, A2, A0, 4, 64, 1e-6, None) == 3                  # dx aliases x
+    assert L.rmsnorm_bwd(A0, A1, A2, A3, 4, 0, 1e-6, None) == 1
+    assert L.linear_bwd(A0, A1, A2, None, None, 4, 4, 4, None) == 1
+    assert L.linear_bwd(A0, A1, A2, A0, None, 4, 4, 4, None) == 3
+    assert L.rope_rmsnorm_res_bwd(A0, 1.0, A1, A2, A3, A4, 4, 64, 128, 0, 1e4, 0, 1e-6, None) == 2  # row > 4096
+
+
+def test_layer_validation_codes():
+    L = vtb.lib()
+    cfg = vtb.make_layer_cfg(8, 2, 96, 0.1)
+    sv = vtb.LayerSaved(A0, A1, A2, A3, A4, A5, A6, WS)
+    assert L.layer_bwd(ctypes.byref(cfg), ctypes.byref(sv), A0 + 0x1000000, A1 + 0x1000000, A2 + 0x1000000,
+                       A3 + 0x1000000, A4 + 0x1000000, WS + 0x1000000, 1 << 30, None) == 2
+    cfg = vtb.make_layer_cfg(8, 2, 64, 0.1)
+    assert L.layer_bwd(ctypes.byref(cfg), None, A0, A1, A2, A3, A4, WS, 1 << 30, None) == 1
+    assert vtb.layer_bwd_workspace_size(cfg) > 0

@@ -1,0 +1,173 @@
+"""GPU parity of attn_bwd / attn_fwd_lse (through the C ABI) against the float64 oracle."""
+
+import functools
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import verified_transformer_backward_amd as vtb
+from oracle import attention as A
+from tests.gpu_helpers import TOL, assert_close, dev, host, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, dtype, scale, causal, lse=None, P=None, out_dtype=None, layout="bthd"):
+    need_gpu()
+    t = {n: dev(x[n], dtype) for n in ("q", "k", "v", "dout")}
+    if layout == "bhtd":  # same values, head-major storage: strided [B, T, H, D] views
+        t = {n: v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for n, v in t.items()}
+    od = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    lse_t = None if lse is None else dev(lse)
+    P_t = None if P is None else dev(P)
+    dq, dk, dv = vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], scale, causal, lse=lse_t, P=P_t, out_dtype=od)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+def _check(name, got, ref, tol):
+    for n, g, r in zip(("dq", "dk", "dv"), got, ref):
+        e = assert_close(f"{name}.{n}", g, r, tol)
+        say(f"{name}.{n} rel_err={e:.2e}")
+
+
+def test_tiny_single_query():
+    say("tiny single-query d64 Tk16 fp32, no lse (decode path)")
+    t = synth.tiny_inputs()
+    got = _run(t, "f32", t["scale"], False)
+    ref = A.attention_backward(t["q"], t["k"], t["v"], t["dout"], t["scale"], False)
+    _check("tiny", got, ref, TOL["f32"])
+
+
+def test_decode_gqa_full_size():
+    say("decode GQA B8 Hq20 Hkv5 Tk1024 d128 fp32, no lse")
+    x = synth.decode_gqa_inputs()
+    got = _run(x, "f32", x["scale"], False)
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], x["scale"], False)
+    _check("decode_gqa", got, ref, TOL["f32"])
+
+
+def test_decode_gqa_with_given_lse():
+    say("decode GQA with lse given")
+    x = synth.decode_gqa_inputs()
+    lse = A.attention_lse(x["q"], x["k"], x["scale"], False)
+    got = _run(x, "f32", x["scale"], False, lse=lse.astype(np.float32))
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], x["scale"], False, lse=lse.astype(np.float32))
+    _check("decode_gqa_lse", got, ref, TOL["f32"])
+
+
+@functools.lru_cache(maxsize=1)
+def _causal_train_oracle():
+    x = synth.causal_inputs()
+    lse = A.attention_lse(x["q"], x["k"], x["scale"], True).astype(np.float32)
+    return x, lse, A.attention_backward(x["q"], x["k"], x["v"], x["dout"], x["scale"], True, lse=lse)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_causal_train_full_size(out_dtype):
+    say(f"causal B4 H20 T512 d128 bf16, lse given, out {out_dtype}")
+    x, lse, ref = _causal_train_oracle()
+    got = _run(x, "bf16", x["scale"], True, lse=lse, out_dtype=out_dtype)
+    _check(f"causal_train_{out_dtype}", got, ref, TOL["bf16"])
+
+
+def test_causal_train_lse_forward():
+    need_gpu()
+    say("attn_fwd_lse causal B4 H20 T512 d128 bf16")
+    x = synth.causal_inputs()
+    lse = vtb.attn_fwd_lse(dev(x["q"], "bf16"), dev(x["k"], "bf16"), x["scale"], True)
+    torch.cuda.synchronize()
+    ref = A.attention_lse(x["q"], x["k"], x["scale"], True)
+    # lse is an fp32 statistic of exact inputs: judged on the fp32 bar
+    assert_close("lse", host(lse), ref, TOL["f32"])
+
+
+def test_long_causal_full_size_sampled_heads():
+    need_gpu()
+    say("long causal B1 H32 T8192 d128 bf16; oracle on head 17, properties on all")
+    x = synth.long_causal_inputs()
+    sc = x["scale"]
+    heads = [17]
+    lse_o = A.attention_lse(x["q"], x["k"], sc, True, q_heads=heads).astype(np.float32)
+    t = {n: dev(x[n], "bf16") for n in ("q", "k", "v", "dout")}
+    lse = vtb.attn_fwd_lse(t["q"], t["k"], sc, True)     # heads outside the sample use the library's lse
+    for h in heads:
+        lse[:, h] = torch.from_numpy(lse_o[:, h]).cuda()
+    dq, dk, dv = vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, True, lse=lse)
+    torch.cuda.synchronize()
+    say("long causal: GPU done, oracle on sampled heads")
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, lse=lse_o, kv_heads=heads)
+    for n, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        e = assert_close(f"long.{n}", host(g[:, :, heads]), r, TOL["bf16"])
+        say(f"long.{n} rel_err={e:.2e}")
+    # every head: <dQ, Q> = <dK, K> (both equal sum dS o S), outputs finite
+    for h in range(32):
+        a = float((dq[0, :, h].float() * t["q"][0, :, h].float()).sum())
+        b = float((dk[0, :, h].float() * t["k"][0, :, h].float()).sum())
+        ref_mag = float(dq[0, :, h].float().abs().sum() * t["q"][0, :, h].float().abs().max())
+        assert abs(a - b) <= 2e-2 * ref_mag, (h, a, b)
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+
+
+CASES = [
+    # name, B, Tq, Tk, Hq, Hkv, D, dtype, causal
+    ("bf16_causal_ragged", 2, 200, 200, 3, 3, 128, "bf16", True),
+    ("bf16_noncausal_gqa_TqltTk", 1, 77, 300, 8, 2, 128, "bf16", False),
+    ("bf16_causal_gqa_TqltTk_d64", 2, 100, 164, 4, 1, 64, "bf16", True),
+    ("f32_causal_d64", 1, 96, 96, 2, 2, 64, "f32", True),
+    ("f32_noncausal_gqa_d128", 2, 40, 70, 8, 2, 128, "f32", False),
+    ("f32_decode_causal_Tq2", 3, 2, 100, 8, 2, 128, "f32", True),
+    ("bf16_decode_Tq1_d64", 2, 1, 257, 4, 4, 64, "bf16", False),
+    ("bf16_single_key", 1, 1, 1, 2, 2, 64, "bf16", True),
+    ("f32_causal_T33", 1, 33, 33, 1, 1, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_edge_shapes(case):
+    name, B, Tq, Tk, Hq, Hkv, D, dtype, causal = case
+    say(f"edge {name}")
+    x = synth.attention_inputs(B, Tq, Tk, Hq, Hkv, D, dtype, seed=zlib.crc32(name.encode()) % 100000)
+    sc = 1.0 / np.sqrt(D)
+    lse = A.attention_lse(x["q"], x["k"], sc, causal).astype(np.float32)
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal, lse=lse)
+    got = _run(x, dtype, sc, causal, lse=lse)
+    _check(name, got, ref, TOL[dtype])
+    got2 = _run(x, dtype, sc, causal, lse=None)        # lse computed inside
+    _check(name + "_nolse", got2, ref, TOL[dtype])
+
+
+def test_strided_head_major_layout():
+    say("bf16 causal, head-major strides")
+    x = synth.attention_inputs(2, 130, 130, 4, 4, 128, "bf16", seed=77)
+    sc = 1.0 / np.sqrt(128)
+    lse = A.attention_lse(x["q"], x["k"], sc, True).astype(np.float32)
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, lse=lse)
+    got = _run(x, "bf16", sc, True, lse=lse, layout="bhtd")
+    _check("bhtd", got, ref, TOL["bf16"])
+
+
+def test_saved_softmax_mode_f32():
+    say("f32 causal with saved P")
+    x = synth.attention_inputs(1, 70, 70, 3, 3, 128, "f32", seed=5)
+    sc = 1.0 / np.sqrt(128)
+    _, _, P = A.attention_forward(x["q"], x["k"], x["v"], sc, True, want_p=True)
+    P32 = P.astype(np.float32)
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, P=P32)
+    got = _run(x, "f32", sc, True, P=P32)
+    _check("saved_P", got, ref, TOL["f32"])
+
+
+def test_no_queries_gives_zero_kv_grads():
+    need_gpu()
+    say("Tq = 0")
+    q = torch.zeros((1, 0, 2, 64), device="cuda")
+    k = torch.randn((1, 5, 2, 64), device="cuda")
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    vtb.attn_bwd(q, k, k.clone(), q.clone(), 0.125, False, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert float(dk.abs().max()) == 0.0 and float(dv.abs().max()) == 0.0

@@ -1,0 +1,157 @@
+"""GPU parity of rope_bwd, rmsnorm_bwd, rope_rmsnorm_res_bwd, linear_bwd and layer_bwd
+(through the C ABI) against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import verified_transformer_backward_amd as vtb
+from oracle import layer as L
+from oracle import specs
+from tests.gpu_helpers import TOL, assert_close, dev, host, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_rope_and_rmsnorm():
+    need_gpu()
+    say("tiny: RoPE 32 pairs pos 5, RMSNorm n 64")
+    t = synth.tiny_inputs()
+    dx = vtb.rope_bwd(dev(t["rope_dy"]), pos0=t["rope_pos"], base=t["rope_base"])
+    ref = L.rope_backward_rows(t["rope_dy"], [t["rope_pos"]], t["rope_base"])
+    assert_close("rope", host(dx), ref, TOL["f32"])
+    th = specs.rope_angles([5], 64)[0]
+    r0, r1 = specs.rope_backward(t["rope_dy"][0, 0, 0::2], t["rope_dy"][0, 0, 1::2], th)
+    assert_close("rope_pairs", host(dx)[0, 0, 0::2], r0, TOL["f32"])
+    assert_close("rope_pairs1", host(dx)[0, 0, 1::2], r1, TOL["f32"])
+    g = vtb.rmsnorm_bwd(dev(t["rms_x"]), dev(t["rms_gamma"]), dev(t["rms_dy"]), t["rms_eps"])
+    ref = specs.rmsnorm_backward(t["rms_x"][0], t["rms_gamma"], t["rms_dy"][0], t["rms_eps"])
+    assert_close("rmsnorm", host(g)[0], ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rope_positions_layouts_inplace(layout):
+    need_gpu()
+    say(f"rope layout {layout}, explicit positions up to 8191, in place")
+    rng = np.random.default_rng(3)
+    T, H, d = 37, 5, 128
+    dy = rng.standard_normal((T, H, d)).astype(np.float32)
+    pos = np.sort(rng.integers(0, 8192, T)).astype(np.int32)
+    ref = L.rope_backward_rows(dy, pos, 10000.0, layout)
+    x = dev(dy)
+    vtb.rope_bwd(x, pos=torch.from_numpy(pos).cuda(), layout=layout, dx=x)
+    torch.cuda.synchronize()
+    assert_close("rope_inplace", host(x), ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("rows,n", [(3, 64), (17, 2560), (5, 5000), (4, 100)])
+def test_rmsnorm_shapes(rows, n):
+    need_gpu()
+    say(f"rmsnorm rows {rows} n {n}")
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    dy = rng.standard_normal((rows, n)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, n).astype(np.float32)
+    out = vtb.rmsnorm_bwd(dev(x), dev(g), dev(dy), 1e-6)
+    torch.cuda.synchronize()
+    assert_close("rmsnorm", host(out), L.rmsnorm_backward_rows(x, g, dy, 1e-6), TOL["f32"])
+
+
+def test_fused_rope_rmsnorm_residual():
+    need_gpu()
+    say("fused rope+rmsnorm+residual T 256 C 2560")
+    rng = np.random.default_rng(4)
+    T, H, d = 256, 20, 128
+    C = H * d
+    dq = rng.standard_normal((T, C)).astype(np.float32)
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    g = rng.standard_normal((T, C)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    sc = 0.25
+    dn = L.rope_backward_rows((sc * dq.astype(np.float64)).reshape(T, H, d), np.arange(T))
+    ref = g + L.rmsnorm_backward_rows(x, gamma, dn.reshape(T, C), 1e-6)
+    out = vtb.rope_rmsnorm_res_bwd(dev(dq), dev(x), dev(gamma), dev(g), H, d, dq_scale=sc)
+    torch.cuda.synchronize()
+    assert_close("fused", host(out), ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("T,K,N", [(100, 72, 50), (64, 64, 64), (256, 2560, 2560), (3, 130, 7)])
+def test_linear_shapes(T, K, N):
+    need_gpu()
+    say(f"linear T {T} K {K} N {N}")
+    rng = np.random.default_rng(T + K + N)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    dy = rng.standard_normal((T, N)).astype(np.float32)
+    dx, dw = vtb.linear_bwd(dev(x), dev(w), dev(dy))
+    torch.cuda.synchronize()
+    rx, rw = L.linear_backward(x, w, dy)
+    assert_close("linear.dx", host(dx), rx, TOL["f32"])
+    assert_close("linear.dw", host(dw), rw, TOL["f32"])
+    # run twice: no atomics, bitwise deterministic
+    dx2, dw2 = vtb.linear_bwd(dev(x), dev(w), dev(dy))
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+
+
+_KEYS = {"x": "x", "gamma": "gamma", "W": "w", "o": "o", "q": "q", "K": "k", "V": "v", "P": "P"}
+
+
+def _saved_to_dev(s):
+    """Oracle saved-tensor names -> the binding's layer_bwd keys, uploaded as fp32."""
+    return {_KEYS[k]: dev(np.ascontiguousarray(v, dtype=np.float32)) for k, v in s.items()}
+
+
+def _layer_case(layer, T, H, d):
+    p = synth.layer_inputs(layer, T=T, H=H, d=d)
+    sc = 1.0 / np.sqrt(d)
+    saved = L.layer_saved(p["h"], p["gamma"], p["K"], p["V"], p["W"], H, sc)
+    saved32 = {k: v.astype(np.float32) for k, v in saved.items()}
+    return saved32, sc
+
+
+@pytest.mark.parametrize("T,H,d", [(64, 2, 64), (100, 3, 128)])
+def test_layer_bwd_small(T, H, d):
+    need_gpu()
+    say(f"layer_bwd T {T} H {H} d {d}")
+    saved, sc = _layer_case(0, T, H, d)
+    g = synth.layer_upstream_grad(T=T, H=H, d=d)
+    ref = L.layer_backward(saved, g, H, sc)
+    sdev = _saved_to_dev(saved)
+    got = vtb.layer_bwd(sdev, dev(g), sc)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("dh_in", "dW", "dK", "dV"), got, ref):
+        e = assert_close(f"layer.{n}", host(a), b, TOL["f32"])
+        say(f"layer.{n} rel_err={e:.2e}")
+
+
+def test_layer_chain_30_layers_full_size():
+    need_gpu()
+    T, H, d, NL = 256, 20, 128, 30
+    say("layer chain: 30 layers T256 C2560, building saved tensors with the oracle forward")
+    saved, sc = [], 1.0 / np.sqrt(d)
+    for l in range(NL):
+        s, _ = _layer_case(l, T, H, d)
+        saved.append(s)
+    g0 = synth.layer_upstream_grad(T=T, H=H, d=d)
+    say("layer chain: GPU backward over 30 layers")
+    g = dev(g0)
+    grads = {}
+    for l in reversed(range(NL)):
+        sd = _saved_to_dev(saved[l])
+        dh_in, dw, dk, dv = vtb.layer_bwd(sd, g, sc)
+        if l in (0, NL - 1):
+            grads[l] = (host(dw), host(dk), host(dv))
+        g = dh_in
+    torch.cuda.synchronize()
+    say("layer chain: oracle backward over 30 layers")
+    gr = g0.astype(np.float64)
+    for l in reversed(range(NL)):
+        gr, dW, dK, dV = L.layer_backward(saved[l], gr, H, sc, want_dw=l in grads)
+        if l in grads:
+            for n, a, b in zip(("dW", "dK", "dV"), grads[l], (dW, dK, dV)):
+                e = assert_close(f"layer{l}.{n}", a, b, TOL["f32"])
+                say(f"layer{l}.{n} rel_err={e:.2e}")
+    e = assert_close("chain.g0", host(g), gr, TOL["f32"])
+    say(f"chain.g0 rel_err={e:.2e}")

@@ -1,0 +1,272 @@
+"""Python binding of libvtb, the MI355X (gfx950) attention-layer backward library.
+
+Argument marshalling only: every computation runs in the library's HIP kernels. PyTorch
+provides device memory (tensors) and the current HIP stream. There is no fallback: if
+libvtb.so is missing or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI in include/vtb.h):
+    attn_bwd, attn_fwd_lse, rope_bwd, rmsnorm_bwd, rope_rmsnorm_res_bwd, linear_bwd,
+    layer_bwd, plus the workspace-size queries.
+Attention tensors use the [B, T, H, D] layout (any strides, D contiguous).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvtb.so")
+
+VTB_F32, VTB_BF16 = 0, 1
+_STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_ALIAS", 4: "VTB_ERR_WORKSPACE", 5: "VTB_ERR_HIP"}
+
+EXPORTS = (
+    "vtb_status_string", "vtb_last_error", "vtb_abi_version",
+    "attn_bwd_workspace_size", "attn_bwd", "attn_fwd_lse",
+    "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd",
+    "layer_bwd_workspace_size", "layer_bwd",
+)
+
+
+class VtbError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {detail}")
+
+
+class AttnBwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("s_q", ctypes.c_int64 * 3), ("s_k", ctypes.c_int64 * 3), ("s_v", ctypes.c_int64 * 3),
+        ("s_do", ctypes.c_int64 * 3), ("s_dq", ctypes.c_int64 * 3), ("s_dk", ctypes.c_int64 * 3),
+        ("s_dv", ctypes.c_int64 * 3),
+    ]
+
+
+class LayerBwdCfg(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("rope_base", ctypes.c_double),
+        ("rope_layout", ctypes.c_int32), ("causal", ctypes.c_int32),
+    ]
+
+
+class LayerSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "gamma", "w", "o", "q", "k", "v", "P")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvtb.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m verified_transformer_backward_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, F64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+    sig = {
+        "vtb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "vtb_last_error": (ctypes.c_char_p, []),
+        "vtb_abi_version": (ctypes.c_int, []),
+        "attn_bwd_workspace_size": (SZ, [ctypes.POINTER(AttnBwdDesc)]),
+        "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
+        "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
+        "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
+        "rope_rmsnorm_res_bwd": (ctypes.c_int, [P, F32, P, P, P, P, I32, I32, I32, I32, F64, I32, F32, P]),
+        "linear_bwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
+        "layer_bwd_workspace_size": (SZ, [ctypes.POINTER(LayerBwdCfg)]),
+        "layer_bwd": (ctypes.c_int, [ctypes.POINTER(LayerBwdCfg), ctypes.POINTER(LayerSaved), P, P, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise VtbError(status, where, lib().vtb_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return VTB_F32
+    if dt == torch.bfloat16:
+        return VTB_BF16
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _bthd_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, T, H, D]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous head dimension")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def make_attn_desc(q, k, scale, causal, out_dtype=None, dout=None, dq=None, dk=None, dv=None, v=None) -> AttnBwdDesc:
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    d = AttnBwdDesc()
+    d.B, d.Hq, d.Hkv, d.Tq, d.Tk, d.D = B, Hq, Hkv, Tq, Tk, D
+    d.scale, d.causal = float(scale), int(bool(causal))
+    d.in_dtype = _dtype_code(q.dtype)
+    d.out_dtype = _dtype_code(out_dtype if out_dtype is not None else q.dtype)
+    for field, t, name in (("s_q", q, "q"), ("s_k", k, "k"), ("s_v", v, "v"), ("s_do", dout, "dout"),
+                           ("s_dq", dq, "dq"), ("s_dk", dk, "dk"), ("s_dv", dv, "dv")):
+        if t is not None:
+            getattr(d, field)[:] = _bthd_strides(t, name)
+    return d
+
+
+def attn_bwd_workspace_size(desc: AttnBwdDesc) -> int:
+    return int(lib().attn_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dtype=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv)."""
+    out_dtype = out_dtype or q.dtype
+    for t, n in ((k, "k"), (v, "v"), (dout, "dout")):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise TypeError(f"{n} must match q's dtype and device")
+    dq = torch.empty(q.shape, dtype=out_dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=out_dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=out_dtype, device=q.device) if dv is None else dv
+    desc = make_attn_desc(q, k, scale, causal, out_dtype, dout, dq, dk, dv, v)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise TypeError("lse must be contiguous float32 [B, Hq, Tq]")
+    if P is not None and (P.dtype != torch.float32 or not P.is_contiguous()):
+        raise TypeError("P must be contiguous float32 [B, Hq, Tq, Tk]")
+    if workspace is None:
+        workspace = _workspace(attn_bwd_workspace_size(desc), q.device)
+    st = lib().attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(P),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_fwd_lse(q, k, scale: float, causal: bool, lse=None, stream=None):
+    """Row log-sum-exp [B, Hq, Tq] (fp32) of the scaled scores over visible keys."""
+    B, Tq, Hq, _ = q.shape
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    desc = make_attn_desc(q, k, scale, causal)
+    _check(lib().attn_fwd_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _stream(stream)), "attn_fwd_lse")
+    return lse
+
+
+def rope_bwd(dy, pos=None, pos0: int = 0, base: float = 10000.0, layout: int = 0, dx=None, stream=None):
+    """R(-theta) on every pair of dy [n_tok, n_heads, head_dim] (fp32, heads packed)."""
+    if dy.dtype != torch.float32 or dy.dim() != 3 or dy.stride(2) != 1 or dy.stride(1) != dy.shape[2]:
+        raise ValueError("dy must be float32 [n_tok, n_heads, head_dim] with packed heads")
+    dx = torch.empty_like(dy) if dx is None else dx
+    if dx.stride() != dy.stride():
+        raise ValueError("dx must have dy's strides")
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
+        raise TypeError("pos must be contiguous int32")
+    n, h, d = dy.shape
+    _check(lib().rope_bwd(_ptr(dy), _ptr(dx), n, h, d, dy.stride(0), _ptr(pos), int(pos0), float(base), int(layout),
+                          _stream(stream)), "rope_bwd")
+    return dx
+
+
+def rmsnorm_bwd(x, gamma, dy, eps: float = 1e-6, dx=None, stream=None):
+    """rmsNormBackward per row of x, dy [rows, n] (fp32 contiguous)."""
+    for t, nm in ((x, "x"), (gamma, "gamma"), (dy, "dy")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be contiguous float32")
+    dx = torch.empty_like(x) if dx is None else dx
+    rows, n = x.shape
+    _check(lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), rows, n, float(eps), _stream(stream)), "rmsnorm_bwd")
+    return dx
+
+
+def rope_rmsnorm_res_bwd(dq, x, gamma, dh_out, n_heads: int, head_dim: int, dq_scale: float = 1.0, pos0: int = 0,
+                         base: float = 10000.0, layout: int = 0, eps: float = 1e-6, dh_in=None, stream=None):
+    """dh_in = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq_scale * dq)) per token row."""
+    for t, nm in ((dq, "dq"), (x, "x"), (gamma, "gamma"), (dh_out, "dh_out")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be contiguous float32")
+    dh_in = torch.empty_like(dh_out) if dh_in is None else dh_in
+    T = dh_out.shape[0]
+    _check(lib().rope_rmsnorm_res_bwd(_ptr(dq), float(dq_scale), _ptr(x), _ptr(gamma), _ptr(dh_out), _ptr(dh_in), T,
+                                      n_heads, head_dim, int(pos0), float(base), int(layout), float(eps),
+                                      _stream(stream)), "rope_rmsnorm_res_bwd")
+    return dh_in
+
+
+def linear_bwd(x, w, dy, want_dx: bool = True, want_dw: bool = True, dx=None, dw=None, stream=None):
+    """dX = dY W^T, dW = X^T dY for Y = X W (fp32 contiguous). Returns (dx, dw)."""
+    for t, nm in ((x, "x"), (w, "w"), (dy, "dy")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be contiguous float32")
+    T, K = x.shape
+    N = w.shape[1]
+    if want_dx and dx is None:
+        dx = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    if want_dw and dw is None:
+        dw = torch.empty((K, N), dtype=torch.float32, device=x.device)
+    _check(lib().linear_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx if want_dx else None), _ptr(dw if want_dw else None),
+                            T, K, N, _stream(stream)), "linear_bwd")
+    return (dx if want_dx else None), (dw if want_dw else None)
+
+
+def make_layer_cfg(T, H, D, scale, eps=1e-6, rope_base=10000.0, rope_layout=0, causal=True) -> LayerBwdCfg:
+    c = LayerBwdCfg()
+    c.T, c.H, c.D = T, H, D
+    c.scale, c.eps, c.rope_base = float(scale), float(eps), float(rope_base)
+    c.rope_layout, c.causal = int(rope_layout), int(bool(causal))
+    return c
+
+
+def layer_bwd_workspace_size(cfg: LayerBwdCfg) -> int:
+    return int(lib().layer_bwd_workspace_size(ctypes.byref(cfg)))
+
+
+def layer_bwd(saved: dict, dh_out, scale: float, eps: float = 1e-6, rope_base: float = 10000.0, rope_layout: int = 0,
+              causal: bool = True, dh_in=None, dw=None, dk=None, dv=None, workspace=None, stream=None):
+    """One layer's backward over its saved tensors (x, gamma, w, o, q, k, v, P); returns
+    (dh_in, dw, dk, dv). q, k, v are [T, H, D]; P is [H, T, T]."""
+    T, H, D = saved["q"].shape
+    for n in ("x", "gamma", "w", "o", "q", "k", "v", "P"):
+        t = saved[n]
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"saved[{n!r}] must be contiguous float32")
+    cfg = make_layer_cfg(T, H, D, scale, eps, rope_base, rope_layout, causal)
+    sv = LayerSaved(*[saved[n].data_ptr() for n in ("x", "gamma", "w", "o", "q", "k", "v", "P")])
+    dev = dh_out.device
+    dh_in = torch.empty_like(dh_out) if dh_in is None else dh_in
+    dw = torch.empty_like(saved["w"]) if dw is None else dw
+    dk = torch.empty_like(saved["k"]) if dk is None else dk
+    dv = torch.empty_like(saved["v"]) if dv is None else dv
+    if workspace is None:
+        workspace = _workspace(layer_bwd_workspace_size(cfg), dev)
+    _check(lib().layer_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dh_out), _ptr(dh_in), _ptr(dw), _ptr(dk), _ptr(dv),
+                           _ptr(workspace), workspace.numel(), _stream(stream)), "layer_bwd")
+    return dh_in, dw, dk, dv

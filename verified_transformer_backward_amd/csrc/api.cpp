@@ -1,0 +1,410 @@
+// C ABI of libvtb: argument validation, alias and workspace checks, path selection and
+// launches on the caller's stream. Nothing here allocates device memory or synchronises.
+#include "vtb.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return VTB_OK;
+  return fail(VTB_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+Span span_of(const void* p, size_t bytes) {
+  Span s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + bytes;
+  return s;
+}
+
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Bytes spanned by a [B, T, H, D] tensor with (b, t, h) strides and D contiguous.
+size_t bthd_bytes(int B, int T, int H, int D, const int64_t st[3], size_t esize) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
+  const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(T - 1) * st[1] + (int64_t)(H - 1) * st[2] + D;
+  return (size_t)last * esize;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool valid_dtype(int32_t d) { return d == VTB_F32 || d == VTB_BF16; }
+size_t esize(int32_t d) { return d == VTB_BF16 ? 2 : 4; }
+
+// Workspace carve-up of the flash path: dq accumulator, row term D, computed lse.
+struct FlashWs {
+  size_t dq_acc, dlt, lse, total;
+};
+
+FlashWs flash_ws(const attn_bwd_desc* d) {
+  FlashWs w;
+  const size_t rows = (size_t)d->B * d->Hq * d->Tq;
+  w.dq_acc = 0;
+  w.dlt = align256(rows * d->D * sizeof(float));
+  w.lse = w.dlt + align256(rows * sizeof(float));
+  w.total = w.lse + align256(rows * sizeof(float));
+  return w;
+}
+
+vtb::AttnParams make_params(const attn_bwd_desc* d) {
+  vtb::AttnParams p{};
+  p.B = d->B;
+  p.Hq = d->Hq;
+  p.Hkv = d->Hkv;
+  p.Tq = d->Tq;
+  p.Tk = d->Tk;
+  p.D = d->D;
+  p.scale = d->scale;
+  p.causal = d->causal;
+  p.in_bf16 = d->in_dtype == VTB_BF16;
+  p.out_bf16 = d->out_dtype == VTB_BF16;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = d->s_q[i];
+    p.sk[i] = d->s_k[i];
+    p.sv[i] = d->s_v[i];
+    p.sdo[i] = d->s_do[i];
+    p.sdq[i] = d->s_dq[i];
+    p.sdk[i] = d->s_dk[i];
+    p.sdv[i] = d->s_dv[i];
+  }
+  return p;
+}
+
+// Shape, dtype and stride checks shared by attn_bwd, its workspace query and attn_fwd_lse.
+int check_desc(const attn_bwd_desc* d, bool need_grads) {
+  if (!d) return fail(VTB_ERR_ARG, "desc is NULL");
+  if (d->B < 0 || d->Tq < 0 || d->Tk < 0) return fail(VTB_ERR_ARG, "negative size (B=%d Tq=%d Tk=%d)", d->B, d->Tq, d->Tk);
+  if (d->Hq < 1 || d->Hkv < 1) return fail(VTB_ERR_ARG, "Hq=%d and Hkv=%d must be >= 1", d->Hq, d->Hkv);
+  if (d->Hq % d->Hkv) return fail(VTB_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", d->Hq, d->Hkv);
+  if (d->D != 64 && d->D != 128) return fail(VTB_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", d->D);
+  if (!valid_dtype(d->in_dtype)) return fail(VTB_ERR_ARG, "in_dtype=%d", d->in_dtype);
+  if (need_grads && !valid_dtype(d->out_dtype)) return fail(VTB_ERR_ARG, "out_dtype=%d", d->out_dtype);
+  if (!std::isfinite(d->scale)) return fail(VTB_ERR_ARG, "scale is not finite");
+  if (d->causal != 0 && d->causal != 1) return fail(VTB_ERR_ARG, "causal=%d must be 0 or 1", d->causal);
+  if (d->causal && d->Tk < d->Tq) return fail(VTB_ERR_ARG, "causal needs Tk >= Tq (Tq=%d Tk=%d)", d->Tq, d->Tk);
+  if (d->Tk == 0 && d->Tq > 0 && d->B > 0) return fail(VTB_ERR_ARG, "Tk == 0: softmax over no keys is undefined");
+  const int64_t* all[7] = {d->s_q, d->s_k, d->s_v, d->s_do, d->s_dq, d->s_dk, d->s_dv};
+  const char* names[7] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
+  for (int t = 0; t < (need_grads ? 7 : 2); ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (all[t][i] < 0) return fail(VTB_ERR_ARG, "%s stride %d is negative", names[t], i);
+      if (all[t][i] % 8) return fail(VTB_ERR_UNSUPPORTED, "%s stride %d = %lld is not a multiple of 8 elements", names[t], i, (long long)all[t][i]);
+    }
+  return VTB_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vtb_status_string(int status) {
+  switch (status) {
+    case VTB_OK: return "VTB_OK";
+    case VTB_ERR_ARG: return "VTB_ERR_ARG";
+    case VTB_ERR_UNSUPPORTED: return "VTB_ERR_UNSUPPORTED";
+    case VTB_ERR_ALIAS: return "VTB_ERR_ALIAS";
+    case VTB_ERR_WORKSPACE: return "VTB_ERR_WORKSPACE";
+    case VTB_ERR_HIP: return "VTB_ERR_HIP";
+    default: return "VTB_UNKNOWN_STATUS";
+  }
+}
+
+const char* vtb_last_error(void) { return g_last_error.c_str(); }
+
+int vtb_abi_version(void) { return 1; }
+
+size_t attn_bwd_workspace_size(const attn_bwd_desc* d) {
+  if (check_desc(d, true) != VTB_OK) return 0;
+  const vtb::AttnParams p = make_params(d);
+  size_t bytes = flash_ws(d).total;
+  if (vtb::decode_applicable(p)) bytes = std::max(bytes, vtb::decode_workspace_bytes(p));
+  return std::max<size_t>(bytes, 256);
+}
+
+int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
+             const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t ein = esize(d->in_dtype), eout = esize(d->out_dtype);
+  const Span sq = span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein));
+  const Span sk = span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein));
+  const Span sv = span_of(v, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_v, ein));
+  const Span sdo = span_of(dout, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_do, ein));
+  const Span sdq = span_of(dq, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_dq, eout));
+  const Span sdk = span_of(dk, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dk, eout));
+  const Span sdv = span_of(dv, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dv, eout));
+  const size_t rows = (size_t)d->B * d->Hq * d->Tq;
+  const Span slse = span_of(lse, P ? 0 : (lse ? rows * 4 : 0));
+  const Span sP = span_of(P, P ? rows * (size_t)d->Tk * 4 : 0);
+  const Span sws = span_of(workspace, workspace_bytes);
+  const bool has_q = d->B > 0 && d->Tq > 0, has_k = d->B > 0 && d->Tk > 0;
+  if (has_q && (!q || !dout || !dq)) return fail(VTB_ERR_ARG, "q, dout and dq must be non-NULL");
+  if (has_k && (!k || !v || !dk || !dv)) return fail(VTB_ERR_ARG, "k, v, dk and dv must be non-NULL");
+  const void* ptrs[8] = {q, k, v, dout, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  const Span outs[3] = {sdq, sdk, sdv};
+  const Span ins[7] = {sq, sk, sv, sdo, slse, sP, sws};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlap(outs[o], ins[i])) return fail(VTB_ERR_ALIAS, "output %d overlaps an input or the workspace", o);
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o], outs[o2])) return fail(VTB_ERR_ALIAS, "outputs %d and %d overlap", o, o2);
+  }
+  for (int i = 0; i < 6; ++i)
+    if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps an input");
+
+  vtb::AttnParams p = make_params(d);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.P = P;
+
+  if (!has_q) {  // no queries: dK = dV = 0
+    if (!has_k) return VTB_OK;
+    rc = hip_status(vtb::launch_zero_bthd(dk, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dk, s), "zero dk");
+    if (rc) return rc;
+    return hip_status(vtb::launch_zero_bthd(dv, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dv, s), "zero dv");
+  }
+
+  const size_t need = attn_bwd_workspace_size(d);
+  if (!workspace || workspace_bytes < need)
+    return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+
+  if (!P && vtb::decode_applicable(p)) {
+    p.lse = lse;
+    return hip_status(vtb::launch_decode(p, workspace, s), "decode path");
+  }
+  const FlashWs w = flash_ws(d);
+  char* base = reinterpret_cast<char*>(workspace);
+  p.dq_acc = reinterpret_cast<float*>(base + w.dq_acc);
+  p.dlt = reinterpret_cast<float*>(base + w.dlt);
+  int mode;
+  if (P) {
+    mode = vtb::PRE_P_GIVEN;
+  } else if (lse) {
+    p.lse = lse;
+    mode = vtb::PRE_LSE_GIVEN;
+  } else {
+    p.lse_out = reinterpret_cast<float*>(base + w.lse);
+    p.lse = p.lse_out;
+    mode = vtb::PRE_LSE_COMPUTE;
+  }
+  rc = hip_status(vtb::launch_flash_pre(p, mode, s), "flash pre-pass");
+  if (rc) return rc;
+  rc = hip_status(vtb::launch_flash_main(p, s), "flash main pass");
+  if (rc) return rc;
+  return hip_status(vtb::launch_dq_finalize(p, s), "dq finalize");
+}
+
+int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* lse, vtb_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_desc(d, false);
+  if (rc) return rc;
+  const size_t ein = esize(d->in_dtype);
+  const size_t rows = (size_t)d->B * d->Hq * d->Tq;
+  if (rows == 0) return VTB_OK;
+  if (!q || !k || !lse) return fail(VTB_ERR_ARG, "q, k and lse must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(VTB_ERR_UNSUPPORTED, "q and k must be 16-byte aligned");
+  const Span sl = span_of(lse, rows * 4);
+  if (overlap(sl, span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein))) ||
+      overlap(sl, span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein))))
+    return fail(VTB_ERR_ALIAS, "lse overlaps q or k");
+  vtb::AttnParams p = make_params(d);
+  p.q = q;
+  p.k = k;
+  p.lse_out = lse;
+  return hip_status(vtb::launch_flash_pre(p, vtb::PRE_LSE_ONLY, reinterpret_cast<hipStream_t>(stream)), "lse pass");
+}
+
+int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,
+             const int32_t* pos, int32_t pos0, double base, int32_t layout, vtb_stream_t stream) {
+  g_last_error.clear();
+  if (n_tok < 0 || n_heads < 1 || head_dim < 2 || (head_dim & 1))
+    return fail(VTB_ERR_ARG, "bad shape n_tok=%d n_heads=%d head_dim=%d (head_dim must be even)", n_tok, n_heads, head_dim);
+  if (tok_stride < (int64_t)n_heads * head_dim) return fail(VTB_ERR_ARG, "tok_stride < n_heads * head_dim");
+  if (layout != 0 && layout != 1) return fail(VTB_ERR_ARG, "layout=%d must be 0 or 1", layout);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(VTB_ERR_ARG, "base must be positive and finite");
+  if (n_tok == 0) return VTB_OK;
+  if (!dy || !dx) return fail(VTB_ERR_ARG, "dy and dx must be non-NULL");
+  const size_t bytes = ((size_t)(n_tok - 1) * tok_stride + (size_t)n_heads * head_dim) * 4;
+  if (dx != dy && overlap(span_of(dx, bytes), span_of(dy, bytes))) return fail(VTB_ERR_ALIAS, "dx partially overlaps dy");
+  if (pos && (overlap(span_of(pos, n_tok * 4u), span_of(dx, bytes))))
+    return fail(VTB_ERR_ALIAS, "pos overlaps dx");
+  return hip_status(vtb::launch_rope_bwd(dy, dx, n_tok, n_heads, head_dim, tok_stride, pos, pos0, base, layout,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                    "rope_bwd");
+}
+
+int rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int32_t rows, int32_t n, float eps,
+                vtb_stream_t stream) {
+  g_last_error.clear();
+  if (rows < 0 || n < 1) return fail(VTB_ERR_ARG, "bad shape rows=%d n=%d", rows, n);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(VTB_ERR_ARG, "eps must be finite and >= 0");
+  if (rows == 0) return VTB_OK;
+  if (!x || !gamma || !dy || !dx) return fail(VTB_ERR_ARG, "x, gamma, dy and dx must be non-NULL");
+  const size_t bytes = (size_t)rows * n * 4;
+  const Span o = span_of(dx, bytes);
+  if (overlap(o, span_of(x, bytes)) || overlap(o, span_of(dy, bytes)) || overlap(o, span_of(gamma, (size_t)n * 4)))
+    return fail(VTB_ERR_ALIAS, "dx overlaps an input");
+  return hip_status(vtb::launch_rmsnorm_bwd(x, gamma, dy, dx, rows, n, eps, reinterpret_cast<hipStream_t>(stream)),
+                    "rmsnorm_bwd");
+}
+
+int rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const float* gamma, const float* dh_out,
+                         float* dh_in, int32_t T, int32_t n_heads, int32_t head_dim, int32_t pos0, double base,
+                         int32_t layout, float eps, vtb_stream_t stream) {
+  g_last_error.clear();
+  if (T < 0 || n_heads < 1 || head_dim < 2 || (head_dim & 1)) return fail(VTB_ERR_ARG, "bad shape");
+  if ((int64_t)n_heads * head_dim > 4096) return fail(VTB_ERR_UNSUPPORTED, "row width n_heads*head_dim > 4096");
+  if (layout != 0 && layout != 1) return fail(VTB_ERR_ARG, "layout must be 0 or 1");
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(VTB_ERR_ARG, "base must be positive and finite");
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !std::isfinite(dq_scale)) return fail(VTB_ERR_ARG, "eps/dq_scale");
+  if (T == 0) return VTB_OK;
+  if (!dq || !x || !gamma || !dh_out || !dh_in) return fail(VTB_ERR_ARG, "NULL pointer");
+  const size_t C = (size_t)n_heads * head_dim, bytes = (size_t)T * C * 4;
+  const Span o = span_of(dh_in, bytes);
+  if (overlap(o, span_of(dq, bytes)) || overlap(o, span_of(x, bytes)) || overlap(o, span_of(gamma, C * 4)))
+    return fail(VTB_ERR_ALIAS, "dh_in overlaps an input");
+  if (dh_in != dh_out && overlap(o, span_of(dh_out, bytes))) return fail(VTB_ERR_ALIAS, "dh_in partially overlaps dh_out");
+  return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq, dq_scale, x, gamma, dh_out, dh_in, T, n_heads, head_dim, pos0,
+                                                     base, layout, eps, reinterpret_cast<hipStream_t>(stream)),
+                    "rope_rmsnorm_res_bwd");
+}
+
+int linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw, int32_t T, int32_t K, int32_t N,
+               vtb_stream_t stream) {
+  g_last_error.clear();
+  if (T < 0 || K < 1 || N < 1) return fail(VTB_ERR_ARG, "bad shape T=%d K=%d N=%d", T, K, N);
+  if (!dx && !dw) return fail(VTB_ERR_ARG, "dx and dw are both NULL");
+  if (!w || !dy || (dw && !x && T > 0)) return fail(VTB_ERR_ARG, "NULL input");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Span sx = span_of(x, (size_t)T * K * 4), sw = span_of(w, (size_t)K * N * 4), sdy = span_of(dy, (size_t)T * N * 4);
+  const Span sdx = span_of(dx, dx ? (size_t)T * K * 4 : 0), sdw = span_of(dw, dw ? (size_t)K * N * 4 : 0);
+  for (const Span& o : {sdx, sdw})
+    if (overlap(o, sx) || overlap(o, sw) || overlap(o, sdy)) return fail(VTB_ERR_ALIAS, "output overlaps an input");
+  if (overlap(sdx, sdw)) return fail(VTB_ERR_ALIAS, "dx overlaps dw");
+  for (const void* ptr : {(const void*)x, (const void*)w, (const void*)dy, (const void*)dx, (const void*)dw})
+    if (ptr && !aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (T == 0) return dw ? hip_status(vtb::launch_zero_f32(dw, (int64_t)K * N, s), "zero dw") : VTB_OK;
+  return hip_status(vtb::launch_linear_bwd(x, w, dy, dx, dw, T, K, N, s), "linear_bwd");
+}
+
+size_t layer_bwd_workspace_size(const layer_bwd_cfg* c) {
+  if (!c || c->T < 1 || c->H < 1 || (c->D != 64 && c->D != 128)) return 0;
+  const size_t TC = (size_t)c->T * c->H * c->D;
+  return align256(TC * 4) * 2 + align256((size_t)c->H * c->T * 4);
+}
+
+int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out, float* dh_in, float* dw, float* dk,
+              float* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!c || !sv) return fail(VTB_ERR_ARG, "cfg and saved must be non-NULL");
+  if (c->T < 1 || c->H < 1) return fail(VTB_ERR_ARG, "T=%d H=%d must be >= 1", c->T, c->H);
+  if (c->D != 64 && c->D != 128) return fail(VTB_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", c->D);
+  if ((int64_t)c->H * c->D > 4096) return fail(VTB_ERR_UNSUPPORTED, "hidden size H*D > 4096");
+  if (c->causal != 0 && c->causal != 1) return fail(VTB_ERR_ARG, "causal must be 0 or 1");
+  if (c->rope_layout != 0 && c->rope_layout != 1) return fail(VTB_ERR_ARG, "rope_layout must be 0 or 1");
+  if (!std::isfinite(c->scale) || !(c->eps >= 0.f) || !(c->rope_base > 0.0)) return fail(VTB_ERR_ARG, "scale/eps/rope_base");
+  const float* in_ptrs[9] = {sv->x, sv->gamma, sv->w, sv->o, sv->q, sv->k, sv->v, sv->P, dh_out};
+  for (const float* ptr : in_ptrs)
+    if (!ptr) return fail(VTB_ERR_ARG, "a saved tensor or dh_out is NULL");
+  if (!dh_in || !dw || !dk || !dv) return fail(VTB_ERR_ARG, "outputs must be non-NULL");
+  for (const float* ptr : in_ptrs)
+    if (!aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const int T = c->T, H = c->H, D = c->D, C = H * D;
+  const size_t TC = (size_t)T * C * 4;
+  const Span ins[9] = {span_of(sv->x, TC), span_of(sv->gamma, (size_t)C * 4), span_of(sv->w, (size_t)C * C * 4),
+                       span_of(sv->o, TC), span_of(sv->q, TC), span_of(sv->k, TC), span_of(sv->v, TC),
+                       span_of(sv->P, (size_t)H * T * T * 4), span_of(dh_out, TC)};
+  const Span outs[4] = {span_of(dh_in, TC), span_of(dw, (size_t)C * C * 4), span_of(dk, TC), span_of(dv, TC)};
+  const Span sws = span_of(workspace, workspace_bytes);
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 9; ++i) {
+      if (o == 0 && i == 8 && dh_in == dh_out) continue;  // in place allowed
+      if (overlap(outs[o], ins[i])) return fail(VTB_ERR_ALIAS, "output %d overlaps input %d", o, i);
+    }
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(outs[o], outs[o2])) return fail(VTB_ERR_ALIAS, "outputs %d and %d overlap", o, o2);
+    if (overlap(outs[o], sws)) return fail(VTB_ERR_ALIAS, "output %d overlaps the workspace", o);
+  }
+  const size_t need = layer_bwd_workspace_size(c);
+  if (!workspace || workspace_bytes < need)
+    return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+  for (int i = 0; i < 9; ++i)
+    if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps input %d", i);
+
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(workspace);
+  float* d_o = reinterpret_cast<float*>(base);
+  float* dq_acc = reinterpret_cast<float*>(base + align256(TC));
+  float* dlt = reinterpret_cast<float*>(base + 2 * align256(TC));
+
+  // 1. linear backward: dO = dh_out W^T, dW = o^T dh_out
+  int rc = hip_status(vtb::launch_linear_bwd(sv->o, sv->w, dh_out, d_o, dw, T, C, C, s), "layer linear");
+  if (rc) return rc;
+  // 2. attention backward with the saved softmax (fp32; dq left unscaled in dq_acc)
+  vtb::AttnParams p{};
+  p.B = 1;
+  p.Hq = p.Hkv = H;
+  p.Tq = p.Tk = T;
+  p.D = D;
+  p.scale = c->scale;
+  p.causal = c->causal;
+  p.in_bf16 = p.out_bf16 = 0;
+  const int64_t st[3] = {(int64_t)T * C, C, D};
+  for (int i = 0; i < 3; ++i) p.sq[i] = p.sk[i] = p.sv[i] = p.sdo[i] = p.sdq[i] = p.sdk[i] = p.sdv[i] = st[i];
+  p.q = sv->q;
+  p.k = sv->k;
+  p.v = sv->v;
+  p.dout = d_o;
+  p.P = sv->P;
+  p.dq_acc = dq_acc;
+  p.dlt = dlt;
+  p.dk = dk;
+  p.dv = dv;
+  rc = hip_status(vtb::launch_flash_pre(p, vtb::PRE_P_GIVEN, s), "layer attention pre-pass");
+  if (rc) return rc;
+  rc = hip_status(vtb::launch_flash_main(p, s), "layer attention main pass");
+  if (rc) return rc;
+  // 3. dh_in = dh_out + RMSNormBackward(x, gamma, RoPEBackward(scale * dq_acc))
+  return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq_acc, c->scale, sv->x, sv->gamma, dh_out, dh_in, T, H, D, 0,
+                                                     c->rope_base, c->rope_layout, c->eps, s),
+                    "layer rope/rmsnorm/residual");
+}
+
+}  // extern "C"

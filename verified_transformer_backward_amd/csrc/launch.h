@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel translation units.
+// Everything here is already validated by the caller; launchers only compute grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vtb {
+
+// Attention backward problem after validation. Element pointers are typed by in_bf16 /
+// out_bf16; strides are (batch, token, head) in elements with the head dim contiguous.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;   // row log-sum-exp read by the backward (given or workspace)
+  const float* P;     // saved softmax [B, Hq, Tq, Tk] or nullptr
+  float* lse_out;     // where a pre-pass that computes lse writes it
+  float* dlt;         // workspace [B, Hq, Tq]: D_i = rowsum(P o dP)
+  float* dq_acc;      // workspace [B, Tq, Hq, D] fp32 dQ accumulator (unscaled)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Tq, Tk, D;
+  float scale;
+  int causal;
+  int in_bf16, out_bf16;
+  int64_t sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
+};
+
+enum PreMode { PRE_LSE_GIVEN = 0, PRE_LSE_COMPUTE = 1, PRE_LSE_ONLY = 2, PRE_P_GIVEN = 3 };
+
+// Flash-style path (any Tq): pre-pass (row term D, optionally lse; zeroes dq_acc),
+// KV-parallel main pass (dK, dV written, dQ accumulated into dq_acc), dQ finalisation.
+hipError_t launch_flash_pre(const AttnParams& p, int mode, hipStream_t s);
+hipError_t launch_flash_main(const AttnParams& p, hipStream_t s);
+hipError_t launch_dq_finalize(const AttnParams& p, hipStream_t s);
+
+// Decode path (Hq/Hkv * Tq <= 16): split-KV chunk statistics, per-chunk gradients, dQ
+// reduction over chunks. Workspace layout is owned by attn_decode.hip.
+size_t decode_workspace_bytes(const AttnParams& p);
+bool decode_applicable(const AttnParams& p);
+hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s);
+
+// Fill `n` floats with zero (graph-capture safe, no hipMemsetAsync).
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s);
+// Zero a strided [B, T, H, D] tensor of fp32 or bf16 elements.
+hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const int64_t st[3], hipStream_t s);
+
+// Elementwise tail.
+hipError_t launch_rope_bwd(const float* dy, float* dx, int n_tok, int n_heads, int head_dim,
+                           int64_t tok_stride, const int32_t* pos, int pos0, double base,
+                           int layout, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx,
+                              int rows, int n, float eps, hipStream_t s);
+hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x,
+                                       const float* gamma, const float* dh_out, float* dh_in, int T,
+                                       int n_heads, int head_dim, int pos0, double base, int layout,
+                                       float eps, hipStream_t s);
+
+// fp32 MFMA GEMMs of the linear backward (one launch computes both products).
+hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw,
+                             int T, int K, int N, hipStream_t s);
+
+}  // namespace vtb
