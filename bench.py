@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention-layer backward on one MI355X.
+
+One step = one attn_bwd call (row-term pre-pass, KV-parallel main pass, dQ finalisation)
+over the causal training workload B4 H20 T512 d128: q, k, v, dO bf16 ~ N(0, 1), saved
+row log-sum-exp fp32 (from the library's own attn_fwd_lse, computed before timing),
+scale 1/sqrt(128), bf16 outputs with fp32 accumulation. Inputs are resident in HBM
+before the timed region. By default the step rotates over 8 copies of inputs, outputs
+and workspace (~760 MB) so no step finds its data in the 256 MB Infinity Cache ("cold");
+a warm number (one set reused) is reported beside it.
+
+Prints ONE JSON line. `value` is TFLOP/s of the five contractions the method counts
+(S recompute, dP, dQ, dK, dV) on the exact causal triangle: 10 * d * B * H * T(T+1)/2.
+The roofline object is for the dominant kernel (the KV-parallel main pass), timed live
+with HIP events recorded by attn_bwd_timed on the launch stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn-backward TFLOP/s & HBM GB/s at B4·H20·T512·d128; % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+MAIN_KERNEL_SRC = os.path.join(ROOT, "verified_transformer_backward_amd", "csrc", "attn_flash_bwd.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_main_causal_train_B4H20T512d128_pmc.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=8, help="rotating input/output sets (1 = warm only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-baseline sample time")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (one runtime per process)."""
+
+    def __init__(self):
+        import torch
+
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(f.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def workload_numbers(B, T, H, d):
+    pairs = B * H * T * (T + 1) // 2                      # visible (query, key) pairs
+    flops = 10 * d * pairs                                # 5 contractions x 2 d per pair
+    n = B * T * H * d
+    compulsory = 4 * n * 2 + B * H * T * 4 + 3 * n * 2    # q,k,v,dO + lse in, dq,dk,dv bf16 out
+    # main pass: reads q, k, v, dO, lse and the row term D once; writes dk, dv (bf16) and
+    # the fp32 dQ accumulator once
+    main_bytes = 4 * n * 2 + 2 * B * H * T * 4 + 2 * n * 2 + n * 4
+    return flops, compulsory, main_bytes
+
+
+def traffic_from_profile():
+    """HBM bytes per main-pass launch from the committed rocprofv3 counter summary, or None
+    when it is missing or was taken on a different version of the kernel source."""
+    try:
+        rec = json.load(open(PMC_SUMMARY))
+        src = hashlib.sha256(open(MAIN_KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != src:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(x, seconds):
+    """The float64 oracle on the same workload, on this host's cores (a baseline only).
+    Each sampled head's lse comes from the oracle's own forward statistic, outside the timing."""
+    import numpy as np
+    from oracle import attention as A
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    B, T, H, d = x["q"].shape
+    # bounded sample: whole (b, h) heads of the same workload, cycling, until ~`seconds` of work
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    dt, done = 0.0, 0
+    while dt < seconds and done < 20 * len(heads):
+        b, h = heads[done % len(heads)]
+        one = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "dout")}
+        lse = A.attention_lse(one["q"], one["k"], x["scale"], True)
+        t0 = time.perf_counter()
+        A.attention_backward(one["q"], one["k"], one["v"], one["dout"], x["scale"], True, lse=lse)
+        dt += time.perf_counter() - t0
+        done += 1
+    flops = 10 * d * done * T * (T + 1) // 2
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} single-head backwards cycling over the {len(heads)} (b,h) heads of "
+                      f"B{B} H{H} T{T} d{d}, float64 numpy, {dt:.1f} s timed"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import verified_transformer_backward_amd as vtb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    B, T, H, d = 4, 512, 20, 128
+    x = synth.causal_inputs(B, T, H, d)
+    sc = float(x["scale"])
+    flops, compulsory, main_bytes = workload_numbers(B, T, H, d)
+
+    dev = torch.device("cuda:0")
+    base = {n: torch.from_numpy(synth.bf16_bits(x[n])).view(torch.bfloat16).to(dev) for n in ("q", "k", "v", "dout")}
+    nsets = max(1, args.sets)
+    sets = []
+    for s in range(nsets):
+        t = {n: v.clone() for n, v in base.items()}
+        t["lse"] = vtb.attn_fwd_lse(t["q"], t["k"], sc, True)
+        t["dq"] = torch.empty_like(t["q"])
+        t["dk"] = torch.empty_like(t["k"])
+        t["dv"] = torch.empty_like(t["v"])
+        desc = vtb.make_attn_desc(t["q"], t["k"], sc, True, torch.bfloat16, t["dout"], t["dq"], t["dk"], t["dv"], t["v"])
+        t["ws"] = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+        sets.append(t)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(t, events=None):
+        vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, True, lse=t["lse"], dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                     workspace=t["ws"], stream=stream, events=events)
+
+    def timed(nsteps, rot):
+        phase = hip.create(4 * nsteps)
+        start, stop = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(start, sptr)
+        for i in range(nsteps):
+            step(sets[i % rot], phase[4 * i:4 * i + 4])
+        hip.record(stop, sptr)
+        torch.cuda.synchronize()
+        total = hip.ms(start, stop)
+        per = {k: [] for k in ("pre", "main", "final")}
+        for i in range(nsteps):
+            e = phase[4 * i:4 * i + 4]
+            per["pre"].append(hip.ms(e[0], e[1]))
+            per["main"].append(hip.ms(e[1], e[2]))
+            per["final"].append(hip.ms(e[2], e[3]))
+        hip.destroy(phase + [start, stop])
+        return total / nsteps, {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    ms_step, kern_us = timed(args.steps, nsets)
+    warm_ms, warm_us = timed(max(10, args.steps // 2), 1)
+
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    main_s = kern_us["main"] * 1e-6
+    achieved = main_bytes / main_s / 1e9
+    traffic = traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal attention backward B4 H20 T512 d128, bf16 in/out, fp32 accumulation, "
+                               "lse given, scale 1/sqrt(128)",
+                   "B": B, "H": H, "T": T, "d": d,
+                   "cache": f"cold: {nsets} rotating input/output sets" if nsets > 1 else "warm"},
+        "hbm_gbps": round(compulsory / (ms_step * 1e-3) / 1e9, 1),
+        "frac_bf16_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "warm": {"ms_per_step": round(warm_ms, 5), "value": round(flops / (warm_ms * 1e-3) / 1e12, 2),
+                 "kernel_us": {k: round(v, 2) for k, v in warm_us.items()}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "flash_main_kernel<bf16, 128, 2, false>",
+                     "algorithmic_bytes": main_bytes,
+                     "mfma_tflops": round(flops / main_s / 1e12, 1)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -91,6 +91,17 @@ int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void
              const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
+/* attn_bwd with phase timing, for measurement: identical work and results, and the
+ * caller's HIP events (hipEvent_t, created by the caller) are recorded on `stream` at
+ * the phase boundaries: events[0] before the first launch, then one event after each
+ * launch (flash path: query-parallel dq pass, key-parallel dk/dv pass, and events[3]
+ * recorded right after events[2]; decode path: chunk statistics, chunk gradients, dQ
+ * reduction). n_events must be >= 4. */
+int attn_bwd_timed(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
+                   const void* dout, const float* lse, const float* P, void* dq, void* dk,
+                   void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream,
+                   void* const* events, int32_t n_events);
+
 /* Forward statistics the backward consumes: lse [B, Hq, Tq] fp32 (written), the row
  * log-sum-exp of the scaled scores over visible keys ("Attention (full single-head)",
  * attentionForward's softmax normaliser). Uses desc's q/k strides, dtypes and mask. */

@@ -26,7 +26,7 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
-    "attn_bwd_workspace_size", "attn_bwd", "attn_fwd_lse",
+    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd",
     "layer_bwd_workspace_size", "layer_bwd",
 )
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "vtb_abi_version": (ctypes.c_int, []),
         "attn_bwd_workspace_size": (SZ, [ctypes.POINTER(AttnBwdDesc)]),
         "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "attn_bwd_timed": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P,
+                                          ctypes.POINTER(ctypes.c_void_p), I32]),
         "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
         "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
         "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
@@ -150,8 +152,11 @@ def attn_bwd_workspace_size(desc: AttnBwdDesc) -> int:
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dtype=None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv)."""
+             dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
+    """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv).
+
+    events: optional sequence of 4 hipEvent_t handles (ints) recorded at the phase
+    boundaries (attn_bwd_timed)."""
     out_dtype = out_dtype or q.dtype
     for t, n in ((k, "k"), (v, "v"), (dout, "dout")):
         if t.dtype != q.dtype or t.device != q.device:
@@ -166,9 +171,13 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dt
         raise TypeError("P must be contiguous float32 [B, Hq, Tq, Tk]")
     if workspace is None:
         workspace = _workspace(attn_bwd_workspace_size(desc), q.device)
-    st = lib().attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(P),
-                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "attn_bwd")
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(P),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib().attn_bwd(*args), "attn_bwd")
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().attn_bwd_timed(*args, arr, len(events)), "attn_bwd_timed")
     return dq, dk, dv
 
 

@@ -57,17 +57,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 bool valid_dtype(int32_t d) { return d == VTB_F32 || d == VTB_BF16; }
 size_t esize(int32_t d) { return d == VTB_BF16 ? 2 : 4; }
 
-// Workspace carve-up of the flash path: dq accumulator, row term D, computed lse.
+// Workspace carve-up of the flash path: row term D, computed lse.
 struct FlashWs {
-  size_t dq_acc, dlt, lse, total;
+  size_t dlt, lse, total;
 };
 
 FlashWs flash_ws(const attn_bwd_desc* d) {
   FlashWs w;
   const size_t rows = (size_t)d->B * d->Hq * d->Tq;
-  w.dq_acc = 0;
-  w.dlt = align256(rows * d->D * sizeof(float));
-  w.lse = w.dlt + align256(rows * sizeof(float));
+  w.dlt = 0;
+  w.lse = align256(rows * sizeof(float));
   w.total = w.lse + align256(rows * sizeof(float));
   return w;
 }
@@ -149,12 +148,28 @@ size_t attn_bwd_workspace_size(const attn_bwd_desc* d) {
   return std::max<size_t>(bytes, 256);
 }
 
-int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
-             const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Records events[i] (when present) on stream s; phase boundaries of attn_bwd.
+struct PhaseEvents {
+  void* const* ev;
+  int n;
+  int next;
+  int mark(hipStream_t s) {
+    if (!ev || next >= n) return VTB_OK;
+    const hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(ev[next++]), s);
+    return hip_status(e, "hipEventRecord");
+  }
+};
+
+int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                  const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t s,
+                  PhaseEvents ev) {
   g_last_error.clear();
   int rc = check_desc(d, true);
   if (rc) return rc;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t ein = esize(d->in_dtype), eout = esize(d->out_dtype);
   const Span sq = span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein));
   const Span sk = span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein));
@@ -205,30 +220,52 @@ int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
   if (!workspace || workspace_bytes < need)
     return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
 
+  if ((rc = ev.mark(s))) return rc;
   if (!P && vtb::decode_applicable(p)) {
     p.lse = lse;
-    return hip_status(vtb::launch_decode(p, workspace, s), "decode path");
+    rc = hip_status(vtb::launch_decode(p, workspace, s), "decode path");
+    if (rc) return rc;
+    return ev.mark(s);
   }
   const FlashWs w = flash_ws(d);
   char* base = reinterpret_cast<char*>(workspace);
-  p.dq_acc = reinterpret_cast<float*>(base + w.dq_acc);
   p.dlt = reinterpret_cast<float*>(base + w.dlt);
   int mode;
   if (P) {
-    mode = vtb::PRE_P_GIVEN;
+    mode = vtb::ROW_P_GIVEN;
   } else if (lse) {
     p.lse = lse;
-    mode = vtb::PRE_LSE_GIVEN;
+    mode = vtb::ROW_LSE_GIVEN;
   } else {
     p.lse_out = reinterpret_cast<float*>(base + w.lse);
     p.lse = p.lse_out;
-    mode = vtb::PRE_LSE_COMPUTE;
+    mode = vtb::ROW_LSE_COMPUTE;
   }
-  rc = hip_status(vtb::launch_flash_pre(p, mode, s), "flash pre-pass");
-  if (rc) return rc;
-  rc = hip_status(vtb::launch_flash_main(p, s), "flash main pass");
-  if (rc) return rc;
-  return hip_status(vtb::launch_dq_finalize(p, s), "dq finalize");
+  rc = hip_status(vtb::launch_flash_dq(p, mode, s), "flash dq pass");
+  if (rc || (rc = ev.mark(s))) return rc;
+  rc = hip_status(vtb::launch_flash_dkdv(p, s), "flash dk/dv pass");
+  if (rc || (rc = ev.mark(s))) return rc;
+  return ev.mark(s);   // two launches on this path: the last two events coincide
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
+             const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
+                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0, 0});
+}
+
+int attn_bwd_timed(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout,
+                   const float* lse, const float* P, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, vtb_stream_t stream, void* const* events, int32_t n_events) {
+  if (!events || n_events < 4) return fail(VTB_ERR_ARG, "attn_bwd_timed needs 4 events");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(VTB_ERR_ARG, "event %d is NULL", i);
+  return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
+                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{events, 4, 0});
 }
 
 int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* lse, vtb_stream_t stream) {
@@ -248,7 +285,7 @@ int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* ls
   p.q = q;
   p.k = k;
   p.lse_out = lse;
-  return hip_status(vtb::launch_flash_pre(p, vtb::PRE_LSE_ONLY, reinterpret_cast<hipStream_t>(stream)), "lse pass");
+  return hip_status(vtb::launch_flash_dq(p, vtb::ROW_LSE_ONLY, reinterpret_cast<hipStream_t>(stream)), "lse pass");
 }
 
 int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,
@@ -327,7 +364,7 @@ int linear_bwd(const float* x, const float* w, const float* dy, float* dx, float
 size_t layer_bwd_workspace_size(const layer_bwd_cfg* c) {
   if (!c || c->T < 1 || c->H < 1 || (c->D != 64 && c->D != 128)) return 0;
   const size_t TC = (size_t)c->T * c->H * c->D;
-  return align256(TC * 4) * 2 + align256((size_t)c->H * c->T * 4);
+  return align256(TC * 4) * 2 + align256((size_t)c->H * c->T * 4);   // dO, dq, row term D
 }
 
 int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out, float* dh_in, float* dw, float* dk,
@@ -371,13 +408,13 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(workspace);
   float* d_o = reinterpret_cast<float*>(base);
-  float* dq_acc = reinterpret_cast<float*>(base + align256(TC));
+  float* dq = reinterpret_cast<float*>(base + align256(TC));
   float* dlt = reinterpret_cast<float*>(base + 2 * align256(TC));
 
   // 1. linear backward: dO = dh_out W^T, dW = o^T dh_out
   int rc = hip_status(vtb::launch_linear_bwd(sv->o, sv->w, dh_out, d_o, dw, T, C, C, s), "layer linear");
   if (rc) return rc;
-  // 2. attention backward with the saved softmax (fp32; dq left unscaled in dq_acc)
+  // 2. attention backward with the saved softmax (fp32; dq = scale dS K into the workspace)
   vtb::AttnParams p{};
   p.B = 1;
   p.Hq = p.Hkv = H;
@@ -393,16 +430,16 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   p.v = sv->v;
   p.dout = d_o;
   p.P = sv->P;
-  p.dq_acc = dq_acc;
+  p.dq = dq;
   p.dlt = dlt;
   p.dk = dk;
   p.dv = dv;
-  rc = hip_status(vtb::launch_flash_pre(p, vtb::PRE_P_GIVEN, s), "layer attention pre-pass");
+  rc = hip_status(vtb::launch_flash_dq(p, vtb::ROW_P_GIVEN, s), "layer attention dq pass");
   if (rc) return rc;
-  rc = hip_status(vtb::launch_flash_main(p, s), "layer attention main pass");
+  rc = hip_status(vtb::launch_flash_dkdv(p, s), "layer attention dk/dv pass");
   if (rc) return rc;
-  // 3. dh_in = dh_out + RMSNormBackward(x, gamma, RoPEBackward(scale * dq_acc))
-  return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq_acc, c->scale, sv->x, sv->gamma, dh_out, dh_in, T, H, D, 0,
+  // 3. dh_in = dh_out + RMSNormBackward(x, gamma, RoPEBackward(dq))
+  return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq, 1.0f, sv->x, sv->gamma, dh_out, dh_in, T, H, D, 0,
                                                      c->rope_base, c->rope_layout, c->eps, s),
                     "layer rope/rmsnorm/residual");
 }

@@ -8,19 +8,21 @@
 // with the causal mask of the DaisyChain-Train transformer.js `backward` (key j visible
 // to query i iff j <= i + Tk - Tq).
 //
-// Three launches:
-//   pre   Q-parallel. Recomputes S and dP over the visible keys of each row and reduces
-//         D_i (and, when no lse is given, lse_i by a lane-local online max/sum merged
-//         across lanes at the end). Zeroes the fp32 dQ accumulator rows it owns.
-//   main  KV-parallel: one workgroup owns BN keys of one kv-head and walks every query
-//         block (of every q-head of the group) that sees them. K and V stay in
-//         registers as MFMA operands; Q and dO tiles are staged in LDS and read both
-//         row-wise (for S, dP) and column-wise through the gfx950 LDS transpose read
-//         (for dK^T += Q^T dS and dV^T += dO^T P), so no transposed copy is stored.
-//         dS goes through LDS once for dQ = dS K; dQ partials are added to the fp32
-//         accumulator with hardware float atomics. dK, dV are summed over the group in a
-//         fixed head order and written once.
-//   final dQ = scale * accumulator, cast to the output type.
+// Two launches, no atomics (results are bitwise reproducible):
+//   dq    query-parallel: sweep 1 over the visible keys reduces D_i (and lse_i when it
+//         is not given); sweep 2 recomputes S and dP, forms dS and accumulates dQ in
+//         registers. Writes dQ and the row term D.
+//   dkdv  key-parallel: recomputes S and dP per query block, forms P and dS and
+//         accumulates dV = P^T dO and dK = scale dS^T Q in registers.
+// S and dP are recomputed once more than a single fused pass would need; in exchange
+// there is no cross-workgroup reduction of dQ.
+//
+// Memory pipeline: every tile is fetched into registers one step ahead with loads that
+// are always in bounds (rows past the end are clamped and zeroed when written to LDS),
+// so no load sits behind a divergent branch and the wait for it falls at its first use.
+// bf16 tiles with 128-element rows use an XOR-swizzled LDS layout that is free of bank
+// conflicts both for the row-wise 16-byte operand reads and for the transpose reads.
+// Both kernels fit 256 registers per lane for bf16, so two workgroups share a CU.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,195 +32,352 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <typename E> constexpr int pad_elems() { return 32 / (int)sizeof(E); }
+// LDS layout of a tile with COLS elements of E per row. 256-byte rows (bf16 x 128) are
+// stored densely with 16-byte chunk c of row r placed at chunk c ^ f(r),
+// f(r) = 2 (r mod 8) + (r / 8 mod 2): any 16 consecutive rows read at one chunk, and any
+// 8 consecutive rows read at two adjacent chunks, touch distinct banks. Other shapes
+// are padded by 32 bytes per row.
+template <typename E, int COLS>
+struct Lds {
+  static constexpr bool kSwz = sizeof(E) == 2 && COLS == 128;
+  static constexpr int LD = kSwz ? COLS : COLS + 32 / (int)sizeof(E);
+  __device__ __forceinline__ static int off(int row, int col) {
+    if constexpr (kSwz) {
+      const int f = ((row & 7) << 1) | ((row >> 3) & 1);
+      return row * COLS + ((((col >> 3) ^ f) << 3) | (col & 7));
+    } else {
+      return row * LD + col;
+    }
+  }
+};
+
+// Unswizzled layout with a given row stride (elements).
+template <int LD_>
+struct Plain {
+  static constexpr int LD = LD_;
+  __device__ __forceinline__ static int off(int row, int col) { return row * LD_ + col; }
+};
 
 template <typename E>
 __device__ __forceinline__ const E* row_ptr(const void* base, const int64_t* st, int b, int t, int h) {
   return reinterpret_cast<const E*>(base) + (int64_t)b * st[0] + (int64_t)t * st[1] + (int64_t)h * st[2];
 }
 
-// Copy `rows` rows of D elements (starting at token t0 of head h) into an LDS tile with
-// row stride LD, zero-filling rows at or beyond `tlimit`.
-template <typename E, int D, int LD>
-__device__ __forceinline__ void stage_rows(E* tile, const void* base, const int64_t* st, int b, int h,
-                                           int t0, int rows, int tlimit) {
-  constexpr int CH = 16 / (int)sizeof(E);  // elements per 16-byte chunk
-  constexpr int CPR = D / CH;
-  for (int idx = threadIdx.x; idx < rows * CPR; idx += kThreads) {
-    const int r = idx / CPR, c = idx % CPR;
-    const int t = t0 + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (t < tlimit) val = *reinterpret_cast<const uint4*>(row_ptr<E>(base, st, b, t, h) + c * CH);
-    *reinterpret_cast<uint4*>(tile + r * LD + c * CH) = val;
+// A ROWS x D tile of one head held in registers, 16 bytes per chunk, spread over the
+// workgroup. load() issues every global load of the tile at once; rows at or beyond
+// tlimit (>= 1) read the last valid row instead and are zeroed by store(), which writes
+// the tile into LDS layout L.
+template <typename E, int D, int ROWS>
+struct TileRegs {
+  static constexpr int CH = 16 / (int)sizeof(E);
+  static constexpr int CPR = D / CH;
+  static constexpr int N = ROWS * CPR / kThreads;
+  static_assert(ROWS * CPR % kThreads == 0, "tile must spread evenly over the workgroup");
+  uint4 v[N];
+  uint32_t valid;
+  __device__ __forceinline__ void load(const void* base, const int64_t* st, int b, int h, int t0, int tlimit) {
+    valid = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int r = idx / CPR, c = idx % CPR;
+      const int t = t0 + r;
+      valid |= (uint32_t)(t < tlimit) << i;
+      v[i] = *reinterpret_cast<const uint4*>(row_ptr<E>(base, st, b, min(t, tlimit - 1), h) + c * CH);
+    }
+  }
+  template <typename L>
+  __device__ __forceinline__ void store(E* tile) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int r = idx / CPR, c = idx % CPR;
+      const bool ok = (valid >> i) & 1u;   // value selects: a select of lvalues would move v[] to scratch
+      const uint4 x = make_uint4(ok ? v[i].x : 0u, ok ? v[i].y : 0u, ok ? v[i].z : 0u, ok ? v[i].w : 0u);
+      *reinterpret_cast<uint4*>(tile + L::off(r, c * CH)) = x;
+    }
+  }
+};
+
+// 8 consecutive row elements (row, col .. col+7) of an LDS tile in layout L.
+template <typename L, typename E>
+__device__ __forceinline__ frag_t<E> row8(const E* tile, int row, int col) {
+  if constexpr (sizeof(E) == 2) {
+    return load8<E>(tile + L::off(row, col));
+  } else {
+    frag_t<E> v;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(tile + L::off(row, col));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(tile + L::off(row, col + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[e + 4] = b[e];
+    }
+    return v;
   }
 }
 
-// ------------------------------------------------------------------------------ pre-pass
-template <typename E, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void flash_pre_kernel(AttnParams p) {
-  constexpr int QT = 2;                    // 16-row query tiles per wave
-  constexpr int BMP = kWaves * QT * 16;    // rows per workgroup
-  constexpr int BNP = 64;                  // keys per staged block
-  constexpr int NKS = D / 32;
-  constexpr int LD = D + pad_elems<E>();
-  constexpr bool kNeedS = MODE != PRE_P_GIVEN;
-  constexpr bool kNeedDP = MODE != PRE_LSE_ONLY;
-  __shared__ __attribute__((aligned(32))) E sK[kNeedS ? BNP * LD : 1];
-  __shared__ __attribute__((aligned(32))) E sV[kNeedDP ? BNP * LD : 1];
+// Column operand: element e of the lane is tile[r0 + e][c] for e < 4 and
+// tile[r1 + e - 4][c] for e >= 4, c = c0 + lane % 16 (r0, r1 may depend on the lane's
+// 16-lane group). bf16 uses the LDS transpose read (see device_common.h).
+template <typename L>
+__device__ __forceinline__ bf16x8 col8(const __bf16* tile, int r0, int r1, int c0) {
+  const int j = threadIdx.x & 15;
+  const __bf16* p0 = tile + L::off(r0 + (j >> 2), c0 + 4 * (j & 3));
+  const __bf16* p1 = tile + L::off(r1 + (j >> 2), c0 + 4 * (j & 3));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+template <typename L>
+__device__ __forceinline__ f32x8 col8(const float* tile, int r0, int r1, int c0) {
+  const int c = c0 + (threadIdx.x & 15);
+  f32x8 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = tile[L::off(r0 + e, c)];
+    v[e + 4] = tile[L::off(r1 + e, c)];
+  }
+  return v;
+}
 
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// ------------------------------------------------------------------------------ dq kernel
+// One workgroup = 64 query rows of one q-head (16 per wave). The wave computes the
+// transposed score tile S^T = K Q^T (keys as rows), so each lane owns one query column:
+// its row statistics are per-lane scalars and dS^T comes out of the MFMA already in the
+// operand order of dQ^T += K^T dS^T.
+//   sweep 1 over visible keys: D = rowsum(P o dP)  (and lse, when not given)
+//   sweep 2 over visible keys: dS = P o (dP - D),  dQ = scale dS K
+template <typename E, int D>
+constexpr int dq_smem_bytes() {
+  constexpr int tiles = 2 * 64 * Lds<E, D>::LD * (int)sizeof(E);   // K and V blocks of 64 keys
+  constexpr int stage = kWaves * 16 * (D + 4) * 4;                   // dQ output staging
+  return tiles > stage ? tiles : stage;
+}
+
+template <typename E, int D, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, sizeof(E) == 2 ? 2 : 1)))
+void flash_dq_kernel(AttnParams p) {
+  using L = Lds<E, D>;
+  constexpr int BM = kWaves * 16;          // query rows per workgroup
+  constexpr int BN = 64;                   // keys per staged block
+  constexpr int NKS = D / 32, NDT = D / 16;
+  constexpr bool kNeedS = MODE != ROW_P_GIVEN;
+  constexpr bool kNeedDP = MODE != ROW_LSE_ONLY;
+  constexpr bool kOnline = MODE == ROW_LSE_COMPUTE || MODE == ROW_LSE_ONLY;
+  __shared__ __attribute__((aligned(32))) char smem[dq_smem_bytes<E, D>()];
+  E* sK = reinterpret_cast<E*>(smem);
+  E* sV = sK + BN * L::LD;
+
+  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const int nqb = (p.Tq + BM - 1) / BM;
+  const int qb = nqb - 1 - (int)blockIdx.y;            // causal: heaviest query block first
   const int G = p.Hq / p.Hkv, kvh = h / G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
-  const int q0 = qb * BMP + w * QT * 16;
   const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
   const float sl2 = p.scale * kLog2e;
+  const int64_t rowbase = ((int64_t)b * p.Hq + h) * Tq;
+  const int qrow = qb * BM + 16 * w + lc;             // this lane's query
+  const int qc = min(qrow, Tq - 1);                    // clamped for loads; never written when >= Tq
+  const bool qok = qrow < Tq;
 
-  frag_t<E> qa[QT][NKS], da[QT][NKS];
+  // Q and dO rows of the lane's query: B operands (k = d, n = query) of S^T and dP^T.
+  frag_t<E> qa[NKS], da[NKS];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int row = q0 + 16 * t + lc;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (kNeedS)
-        qa[t][ks] = row < Tq ? load8<E>(row_ptr<E>(p.q, p.sq, b, row, h) + 32 * ks + 8 * lg) : zero8<E>();
-      if constexpr (kNeedDP)
-        da[t][ks] = row < Tq ? load8<E>(row_ptr<E>(p.dout, p.sdo, b, row, h) + 32 * ks + 8 * lg) : zero8<E>();
-    }
+  for (int ks = 0; ks < NKS; ++ks) {
+    if constexpr (kNeedS) qa[ks] = load8<E>(row_ptr<E>(p.q, p.sq, b, qc, h) + 32 * ks + 8 * lg);
+    if constexpr (kNeedDP) da[ks] = load8<E>(row_ptr<E>(p.dout, p.sdo, b, qc, h) + 32 * ks + 8 * lg);
   }
+  float lrow = MODE == ROW_LSE_GIVEN ? p.lse[rowbase + qc] * kLog2e : 0.f;   // log2-domain lse
 
-  float lse2[QT][4], acc[QT][4], mrun[QT][4], lrun[QT][4], urun[QT][4];
-#pragma unroll
-  for (int t = 0; t < QT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = q0 + 16 * t + 4 * lg + r;
-      lse2[t][r] = (MODE == PRE_LSE_GIVEN && i < Tq) ? p.lse[((int64_t)b * p.Hq + h) * Tq + i] * kLog2e : 0.f;
-      acc[t][r] = 0.f;
-      mrun[t][r] = -INFINITY;
-      lrun[t][r] = 0.f;
-      urun[t][r] = 0.f;
-    }
-
-  const int last_row = min(Tq, (qb + 1) * BMP) - 1;
+  const int last_row = min(Tq, (qb + 1) * BM) - 1;
   const int kend = p.causal ? min(Tk, last_row + off + 1) : Tk;
-  for (int jb = 0; jb < kend; jb += BNP) {
-    __syncthreads();
-    if constexpr (kNeedS) stage_rows<E, D, LD>(sK, p.k, p.sk, b, kvh, jb, BNP, Tk);
-    if constexpr (kNeedDP) stage_rows<E, D, LD>(sV, p.v, p.sv, b, kvh, jb, BNP, Tk);
-    __syncthreads();
-    f32x4 S[QT][4], dP[QT][4];
+  TileRegs<E, D, BN> kt_regs, vt_regs;
+
+  // S^T and dP^T of one staged block: tile kt covers keys jb + 16 kt + 4 lg + r (r = reg).
+  auto block_scores = [&](f32x4 (&sT)[4], f32x4 (&dpT)[4]) {
 #pragma unroll
-    for (int t = 0; t < QT; ++t)
+    for (int kt = 0; kt < 4; ++kt) {
+      sT[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpT[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kNeedS) {
+        frag_t<E> ak[NKS];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        S[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dP[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < NKS; ++ks) ak[ks] = row8<L>(sK, 16 * kt + lc, 32 * ks + 8 * lg);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma(sT[kt], ak[ks], qa[ks]);
       }
+      if constexpr (kNeedDP) {
+        frag_t<E> av[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) av[ks] = row8<L>(sV, 16 * kt + lc, 32 * ks + 8 * lg);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma(dpT[kt], av[ks], da[ks]);
+      }
+    }
+  };
+  // Stage key block jb (already in registers) and start fetching block jb + BN.
+  auto stage_block = [&](int jb) {
+    __syncthreads();
+    kt_regs.template store<L>(sK);   // K: S^T operand and, in sweep 2, the dQ operand
+    if constexpr (kNeedDP) vt_regs.template store<L>(sV);
+    __syncthreads();
+    if (jb + BN < kend) {
+      kt_regs.load(p.k, p.sk, b, kvh, jb + BN, Tk);
+      if constexpr (kNeedDP) vt_regs.load(p.v, p.sv, b, kvh, jb + BN, Tk);
+    }
+  };
+  auto start_sweep = [&]() {
+    if (kend > 0) {
+      kt_regs.load(p.k, p.sk, b, kvh, 0, Tk);
+      if constexpr (kNeedDP) vt_regs.load(p.v, p.sv, b, kvh, 0, Tk);
+    }
+  };
+  auto prob = [&](float s_t, int j) -> float {   // P of (this lane's query, key j), 0 when invisible
+    const bool vis = qok & (j < Tk) & (!p.causal | (j <= qrow + off));
+    if constexpr (MODE == ROW_P_GIVEN) {
+      const float pv = p.P[(rowbase + qc) * Tk + min(j, Tk - 1)];
+      return vis ? pv : 0.f;
+    } else {
+      const float pe = __builtin_amdgcn_exp2f(s_t * sl2 - lrow);
+      return vis ? pe : 0.f;
+    }
+  };
+
+  // ---- sweep 1: row term D (and lse)
+  float accd = 0.f, mrun = -INFINITY, lrun = 0.f, urun = 0.f;
+  start_sweep();
+  for (int jb = 0; jb < kend; jb += BN) {
+    stage_block(jb);
+    f32x4 sT[4], dpT[4];
+    block_scores(sT, dpT);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if constexpr (kNeedS) {
-          const frag_t<E> bk = load8<E>(sK + (16 * kt + lc) * LD + 32 * ks + 8 * lg);
-#pragma unroll
-          for (int t = 0; t < QT; ++t) mma(S[t][kt], qa[t][ks], bk);
-        }
-        if constexpr (kNeedDP) {
-          const frag_t<E> bv = load8<E>(sV + (16 * kt + lc) * LD + 32 * ks + 8 * lg);
-#pragma unroll
-          for (int t = 0; t < QT; ++t) mma(dP[t][kt], da[t][ks], bv);
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + 16 * kt + 4 * lg + r;
+        if constexpr (kOnline) {
+          const bool vis = qok & (j < Tk) & (!p.causal | (j <= qrow + off));
+          const float s2 = vis ? sT[kt][r] * sl2 : -INFINITY;
+          const float mn = fmaxf(mrun, s2);
+          const float a = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun - mn);
+          const float e = vis ? __builtin_amdgcn_exp2f(s2 - mn) : 0.f;
+          lrun = lrun * a + e;
+          if constexpr (kNeedDP) urun = urun * a + e * dpT[kt][r];
+          mrun = mn;
+        } else {
+          accd += prob(sT[kt][r], j) * dpT[kt][r];
         }
       }
+  }
+  // combine the four 16-lane groups that hold the same query
+  float drow;
+  if constexpr (kOnline) {
+    float M = fmaxf(mrun, __shfl_xor(mrun, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    const float sc = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
+    float Ls = lrun * sc, U = urun * sc;
+    Ls += __shfl_xor(Ls, 16, 64);
+    Ls += __shfl_xor(Ls, 32, 64);
+    U += __shfl_xor(U, 16, 64);
+    U += __shfl_xor(U, 32, 64);
+    lrow = M + log2f(Ls);
+    drow = U / Ls;
+    if (lg == 0 && qok) p.lse_out[rowbase + qrow] = lrow * kLn2;
+  } else {
+    drow = accd + __shfl_xor(accd, 16, 64);
+    drow += __shfl_xor(drow, 32, 64);
+  }
+  if constexpr (MODE == ROW_LSE_ONLY) {
+    return;
+  } else {
+    if (lg == 0 && qok) p.dlt[rowbase + qrow] = drow;
+
+    // ---- sweep 2: dQ^T += K^T dS^T
+    f32x4 dqT[NDT];
 #pragma unroll
-    for (int t = 0; t < QT; ++t)
+    for (int dt = 0; dt < NDT; ++dt) dqT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    start_sweep();
+    for (int jb = 0; jb < kend; jb += BN) {
+      stage_block(jb);
+      f32x4 sT[4], dpT[4];
+      block_scores(sT, dpT);
+      frag_t<E> dsb[2];   // keys 32c + 4lg + (0..3) and 32c + 16 + 4lg + (0..3)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = q0 + 16 * t + 4 * lg + r;
-          const int j = jb + 16 * kt + lc;
-          const bool vis = i < Tq && j < Tk && (!p.causal || j <= i + off);
-          if constexpr (MODE == PRE_LSE_GIVEN) {
-            const float pr = vis ? exp2f(S[t][kt][r] * sl2 - lse2[t][r]) : 0.f;
-            acc[t][r] += pr * dP[t][kt][r];
-          } else if constexpr (MODE == PRE_P_GIVEN) {
-            const float pr = vis ? p.P[(((int64_t)b * p.Hq + h) * Tq + i) * Tk + j] : 0.f;
-            acc[t][r] += pr * dP[t][kt][r];
-          } else {
-            if (vis) {
-              const float s2 = S[t][kt][r] * sl2;
-              const float mn = fmaxf(mrun[t][r], s2);
-              const float a = exp2f(mrun[t][r] - mn);
-              const float e = exp2f(s2 - mn);
-              lrun[t][r] = lrun[t][r] * a + e;
-              if constexpr (MODE == PRE_LSE_COMPUTE) urun[t][r] = urun[t][r] * a + e * dP[t][kt][r];
-              mrun[t][r] = mn;
-            }
-          }
+          const int j = jb + 16 * kt + 4 * lg + r;
+          const float ds = prob(sT[kt][r], j) * (dpT[kt][r] - drow);
+          dsb[kt >> 1][4 * (kt & 1) + r] = from_f32<E>(ds);
         }
-  }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) mma(dqT[dt], col8<L>(sK, 32 * c + 4 * lg, 32 * c + 16 + 4 * lg, 16 * dt), dsb[c]);
+    }
 
+    // dQ = scale dQ^T, transposed to query-major rows through LDS, then row stores.
+    __syncthreads();
+    float* stage = reinterpret_cast<float*>(smem) + w * 16 * (D + 4);
 #pragma unroll
-  for (int t = 0; t < QT; ++t)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = q0 + 16 * t + 4 * lg + r;
-      const int64_t ri = ((int64_t)b * p.Hq + h) * Tq + i;
-      if constexpr (MODE == PRE_LSE_GIVEN || MODE == PRE_P_GIVEN) {
-        const float dsum = group16_sum(acc[t][r]);
-        if (lc == 0 && i < Tq) p.dlt[ri] = dsum;
+      for (int r = 0; r < 4; ++r) stage[lc * (D + 4) + 16 * dt + 4 * lg + r] = dqT[dt][r] * p.scale;
+    __syncthreads();
+    const int rl = lane >> 2;
+    const int qo = qb * BM + 16 * w + rl;
+    if (qo < Tq) {
+      const int64_t o = (int64_t)b * p.sdq[0] + (int64_t)qo * p.sdq[1] + (int64_t)h * p.sdq[2];
+      const float* src = stage + rl * (D + 4);
+      constexpr int PER = D / 4;
+      const int c0 = (lane & 3) * PER;
+      if (p.out_bf16) {
+        __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + o;
+#pragma unroll
+        for (int c = 0; c < PER; c += 8) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[c0 + c + e];
+          *reinterpret_cast<bf16x8*>(dst + c0 + c) = v;
+        }
       } else {
-        const float M = group16_max(mrun[t][r]);
-        const float sc = mrun[t][r] == -INFINITY ? 0.f : exp2f(mrun[t][r] - M);
-        const float L = group16_sum(lrun[t][r] * sc);
-        if (lc == 0 && i < Tq) {
-          p.lse_out[ri] = (M + log2f(L)) * kLn2;
-        }
-        if constexpr (MODE == PRE_LSE_COMPUTE) {
-          const float U = group16_sum(urun[t][r] * sc);
-          if (lc == 0 && i < Tq) p.dlt[ri] = U / L;
-        }
+        float* dst = reinterpret_cast<float*>(p.dq) + o;
+#pragma unroll
+        for (int c = 0; c < PER; c += 4)
+          *reinterpret_cast<float4*>(dst + c0 + c) = make_float4(src[c0 + c], src[c0 + c + 1], src[c0 + c + 2], src[c0 + c + 3]);
       }
     }
-
-  if constexpr (MODE != PRE_LSE_ONLY) {
-    // zero this workgroup's rows of the dQ accumulator
-    constexpr int C4 = D / 4;
-    for (int idx = tid; idx < BMP * C4; idx += kThreads) {
-      const int r = idx / C4, c = idx % C4;
-      const int i = qb * BMP + r;
-      if (i < Tq)
-        *reinterpret_cast<float4*>(p.dq_acc + (((int64_t)b * Tq + i) * p.Hq + h) * D + 4 * c) =
-            make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
 }
 
-// ------------------------------------------------------------------------------ main pass
-template <typename E, int D, int KW>
-constexpr int main_smem_kt_bytes() {
-  constexpr int BN = kWaves * 16 * KW;
-  constexpr int a = BN * (D + pad_elems<E>()) * (int)sizeof(E);
-  constexpr int b = kWaves * 16 * (D + 4) * 4;  // epilogue staging
-  return a > b ? a : b;
+// ------------------------------------------------------------------------------ dkdv kernel
+// One workgroup = 64 keys of one kv-head (16 per wave); it walks every query block (of
+// every q-head of the group) that sees them. K and V rows of the wave are B operands in
+// registers; Q and dO tiles go through LDS and are read row-wise (S, dP) and through
+// the LDS transpose read (dV^T += dO^T P, dK^T += Q^T dS). dK, dV are summed over the
+// group in a fixed head order and written once.
+template <typename E, int D>
+constexpr int dkdv_stage_bytes() {
+  return kWaves * 16 * (D + 4) * 4;
 }
 
-template <typename E, int D, int KW, bool PGIVEN>
-__global__ __launch_bounds__(kThreads) void flash_main_kernel(AttnParams p) {
-  constexpr int BN = kWaves * 16 * KW;   // keys per workgroup
+template <typename E, int D, bool PGIVEN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, sizeof(E) == 2 ? 2 : 1)))
+void flash_dkdv_kernel(AttnParams p) {
+  constexpr int BN = kWaves * 16;        // keys per workgroup
   constexpr int BM = 32;                 // query rows per iteration
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  constexpr int NDQ = NDT / 2;           // d tiles of the dQ product per wave
-  constexpr int NC = BN / 32;            // key chunks of the dQ product
-  constexpr int LD = D + pad_elems<E>();
-  constexpr int LDS_S = BN + pad_elems<E>();
-  __shared__ __attribute__((aligned(32))) E sQ[BM * LD];
-  __shared__ __attribute__((aligned(32))) E sdO[BM * LD];
-  __shared__ __attribute__((aligned(32))) E sdS[BM * LDS_S];
-  __shared__ __attribute__((aligned(32))) char smem_kt[main_smem_kt_bytes<E, D, KW>()];
-  __shared__ float sL[BM], sDl[BM];
-  E* sK = reinterpret_cast<E*>(smem_kt);
+  using LQ = Lds<E, D>;
+  constexpr int QBYTES = BM * LQ::LD * (int)sizeof(E);
+  constexpr int SMEM = 2 * QBYTES > dkdv_stage_bytes<E, D>() ? 2 * QBYTES : dkdv_stage_bytes<E, D>();
+  __shared__ __attribute__((aligned(32))) char smem[SMEM];
+  __shared__ __attribute__((aligned(16))) float sL[BM], sDl[BM];
+  E* sQ = reinterpret_cast<E*>(smem);
+  E* sdO = reinterpret_cast<E*>(smem + QBYTES);
 
   const int b = blockIdx.x / p.Hkv, kvh = blockIdx.x % p.Hkv;
   const int kb = blockIdx.y * BN;
@@ -226,249 +385,201 @@ __global__ __launch_bounds__(kThreads) void flash_main_kernel(AttnParams p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
   const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
   const float sl2 = p.scale * kLog2e;
+  const int jl = 16 * w + lc;            // this lane's key within the block
+  const int j = kb + jl;
+  const int jc = min(j, Tk - 1);
 
   // K and V rows of this wave as B operands of S = Q K^T and dP = dO V^T.
-  frag_t<E> kr[KW][NKS], vr[KW][NKS];
+  frag_t<E> kr[NKS], vr[NKS];
 #pragma unroll
-  for (int kt = 0; kt < KW; ++kt) {
-    const int key = kb + (w * KW + kt) * 16 + lc;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (!PGIVEN)
-        kr[kt][ks] = key < Tk ? load8<E>(row_ptr<E>(p.k, p.sk, b, key, kvh) + 32 * ks + 8 * lg) : zero8<E>();
-      vr[kt][ks] = key < Tk ? load8<E>(row_ptr<E>(p.v, p.sv, b, key, kvh) + 32 * ks + 8 * lg) : zero8<E>();
+  for (int ks = 0; ks < NKS; ++ks) {
+    if constexpr (!PGIVEN) {
+      kr[ks] = load8<E>(row_ptr<E>(p.k, p.sk, b, jc, kvh) + 32 * ks + 8 * lg);
+      if (j >= Tk) kr[ks] = zero8<E>();
     }
+    vr[ks] = load8<E>(row_ptr<E>(p.v, p.sv, b, jc, kvh) + 32 * ks + 8 * lg);
+    if (j >= Tk) vr[ks] = zero8<E>();
   }
 
-  // K columns for dQ = dS K: this wave owns query tile tq and d tiles dq0 .. dq0+NDQ-1.
-  stage_rows<E, D, LD>(sK, p.k, p.sk, b, kvh, kb, BN, Tk);
-  __syncthreads();
-  const int tq = w & 1;
-  const int dq0 = (w >> 1) * NDQ;
-  frag_t<E> kq[NDQ][NC];
+  f32x4 adV[NDT], adK[NDT];
 #pragma unroll
-  for (int dd = 0; dd < NDQ; ++dd)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kq[dd][c] = load_col8(sK, LD, 32 * c + 8 * lg, 32 * c + 8 * lg + 4, 16 * (dq0 + dd));
-
-  f32x4 adV[KW][NDT], adK[KW][NDT];
-#pragma unroll
-  for (int kt = 0; kt < KW; ++kt)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      adV[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      adK[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int dt = 0; dt < NDT; ++dt) {
+    adV[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    adK[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int q_first = p.causal ? max(0, kb - off) : 0;
-  for (int hj = 0; hj < G; ++hj) {
-    const int h = kvh * G + hj;
+  const int qb0 = q_first / BM;
+  const int nqb = (Tq + BM - 1) / BM - qb0;       // query blocks per head that see this key block
+  const int n_it = nqb > 0 ? G * nqb : 0;
+  TileRegs<E, D, BM> q_regs, do_regs;
+  float l_reg = 0.f, d_reg = 0.f;
+  auto prefetch = [&](int h, int q0) {
+    q_regs.load(p.q, p.sq, b, h, q0, Tq);
+    do_regs.load(p.dout, p.sdo, b, h, q0, Tq);
+    const int i = min(q0 + (tid & (BM - 1)), Tq - 1);   // in bounds for every thread
+    const int64_t rb = ((int64_t)b * p.Hq + h) * Tq;
+    if constexpr (!PGIVEN) l_reg = p.lse[rb + i];   // scaled by log2(e) when staged: a use
+    d_reg = p.dlt[rb + i];                          // right after the load would wait for it
+  };
+  // (head, query block) of the current and next iteration, advanced without division
+  int h = kvh * G, q0 = qb0 * BM;
+  int hn = h, q0n = q0 + BM;
+  if (q0n >= Tq) {
+    q0n = qb0 * BM;
+    ++hn;
+  }
+  if (n_it > 0) prefetch(h, q0);
+  for (int it = 0; it < n_it; ++it) {
     const int64_t rowbase = ((int64_t)b * p.Hq + h) * Tq;
-    for (int q0 = (q_first / BM) * BM; q0 < Tq; q0 += BM) {
-      __syncthreads();
-      stage_rows<E, D, LD>(sQ, p.q, p.sq, b, h, q0, BM, Tq);
-      stage_rows<E, D, LD>(sdO, p.dout, p.sdo, b, h, q0, BM, Tq);
-      if (tid < BM) {
-        const int i = q0 + tid;
-        sL[tid] = (!PGIVEN && i < Tq) ? p.lse[rowbase + i] * kLog2e : 0.f;
-        sDl[tid] = i < Tq ? p.dlt[rowbase + i] : 0.f;
-      }
-      __syncthreads();
+    __syncthreads();
+    q_regs.template store<LQ>(sQ);
+    do_regs.template store<LQ>(sdO);
+    if (tid < BM) {
+      sL[tid] = l_reg * kLog2e;
+      sDl[tid] = d_reg;
+    }
+    __syncthreads();
+    if (it + 1 < n_it) prefetch(hn, q0n);
 
-      f32x4 S[2][KW], dP[2][KW];
+    // S = Q K^T and dP = dO V^T for this wave's 16 keys (rows: 32 queries)
+    f32x4 S[2], dP[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      frag_t<E> ado[NKS], aq[NKS];
 #pragma unroll
-        for (int kt = 0; kt < KW; ++kt) {
-          S[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dP[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        ado[ks] = row8<LQ>(sdO, 16 * t + lc, 32 * ks + 8 * lg);
+        if constexpr (!PGIVEN) aq[ks] = row8<LQ>(sQ, 16 * t + lc, 32 * ks + 8 * lg);
+      }
+      dP[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const frag_t<E> ado = load8<E>(sdO + (16 * t + lc) * LD + 32 * ks + 8 * lg);
-#pragma unroll
-          for (int kt = 0; kt < KW; ++kt) mma(dP[t][kt], ado, vr[kt][ks]);
-          if constexpr (!PGIVEN) {
-            const frag_t<E> aq = load8<E>(sQ + (16 * t + lc) * LD + 32 * ks + 8 * lg);
-#pragma unroll
-            for (int kt = 0; kt < KW; ++kt) mma(S[t][kt], aq, kr[kt][ks]);
-          }
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        mma(dP[t], ado[ks], vr[ks]);
+        if constexpr (!PGIVEN) mma(S[t], aq[ks], kr[ks]);
+      }
+    }
 
-      // P and dS; element e of the packed operands is query 16*(e/4) + 4*lg + e%4.
-      frag_t<E> pb[KW], sb[KW];
+    // P and dS; element e of the packed operands is query 16*(e/4) + 4*lg + e%4.
+    const f32x4 L0 = *reinterpret_cast<const f32x4*>(sL + 4 * lg);
+    const f32x4 L1 = *reinterpret_cast<const f32x4*>(sL + 16 + 4 * lg);
+    const f32x4 D0 = *reinterpret_cast<const f32x4*>(sDl + 4 * lg);
+    const f32x4 D1 = *reinterpret_cast<const f32x4*>(sDl + 16 + 4 * lg);
+    const bool full = q0 + BM <= Tq && kb + BN <= Tk && (!p.causal || kb + BN - 1 <= q0 + off);
+    frag_t<E> pb, sb;
 #pragma unroll
-      for (int kt = 0; kt < KW; ++kt) {
-        const int j = kb + (w * KW + kt) * 16 + lc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = e >> 2, r = e & 3;
-          const int il = 16 * t + 4 * lg + r;
-          const int i = q0 + il;
-          const bool vis = i < Tq && j < Tk && (!p.causal || j <= i + off);
-          float pr;
-          if constexpr (PGIVEN)
-            pr = vis ? p.P[(rowbase + i) * Tk + j] : 0.f;
-          else
-            pr = vis ? exp2f(S[t][kt][r] * sl2 - sL[il]) : 0.f;
-          const float ds = pr * (dP[t][kt][r] - sDl[il]);
-          pb[kt][e] = from_f32<E>(pr);
-          sb[kt][e] = from_f32<E>(ds);
-          sdS[il * LDS_S + (w * KW + kt) * 16 + lc] = from_f32<E>(ds);
+    for (int e = 0; e < 8; ++e) {
+      const int t = e >> 2, r = e & 3;
+      const int i = q0 + 16 * t + 4 * lg + r;
+      const float lrow = t ? L1[r] : L0[r];
+      const float drow = t ? D1[r] : D0[r];
+      float pr;
+      if constexpr (PGIVEN) {
+        const bool vis = (i < Tq) & (j < Tk) & (!p.causal | (j <= i + off));
+        const float pv = p.P[(rowbase + min(i, Tq - 1)) * Tk + jc];
+        pr = vis ? pv : 0.f;
+      } else {
+        pr = __builtin_amdgcn_exp2f(S[t][r] * sl2 - lrow);
+        if (!full) {
+          const bool vis = (i < Tq) & (j < Tk) & (!p.causal | (j <= i + off));
+          pr = vis ? pr : 0.f;
         }
       }
+      pb[e] = from_f32<E>(pr);
+      sb[e] = from_f32<E>(pr * (dP[t][r] - drow));
+    }
 
-      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
+    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const frag_t<E> ado = load_col8(sdO, LD, 4 * lg, 16 + 4 * lg, 16 * dt);
-        const frag_t<E> aq = load_col8(sQ, LD, 4 * lg, 16 + 4 * lg, 16 * dt);
-#pragma unroll
-        for (int kt = 0; kt < KW; ++kt) {
-          mma(adV[kt][dt], ado, pb[kt]);
-          mma(adK[kt][dt], aq, sb[kt]);
-        }
-      }
-      __syncthreads();
+    for (int dt = 0; dt < NDT; ++dt) {
+      mma(adV[dt], col8<LQ>(sdO, 4 * lg, 16 + 4 * lg, 16 * dt), pb);
+      mma(adK[dt], col8<LQ>(sQ, 4 * lg, 16 + 4 * lg, 16 * dt), sb);
+    }
 
-      // dQ partial for query tile tq, d tiles dq0..: dS (LDS, row-wise) times K columns.
-      f32x4 aq_[NDQ];
-#pragma unroll
-      for (int dd = 0; dd < NDQ; ++dd) aq_[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const frag_t<E> a = load8<E>(sdS + (16 * tq + lc) * LDS_S + 32 * c + 8 * lg);
-#pragma unroll
-        for (int dd = 0; dd < NDQ; ++dd) mma(aq_[dd], a, kq[dd][c]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = q0 + 16 * tq + 4 * lg + r;
-        if (i < Tq) {
-          float* dst = p.dq_acc + (((int64_t)b * Tq + i) * p.Hq + h) * D + 16 * dq0 + lc;
-#pragma unroll
-          for (int dd = 0; dd < NDQ; ++dd) unsafeAtomicAdd(dst + 16 * dd, aq_[dd][r]);
-        }
-      }
+    h = hn;
+    q0 = q0n;
+    q0n += BM;
+    if (q0n >= Tq) {
+      q0n = qb0 * BM;
+      ++hn;
     }
   }
 
-  // Epilogue: stage each 16-key tile through LDS (transposing d-major accumulators to
-  // key-major rows) and write dK = scale * acc, dV = acc with coalesced row stores.
-  __syncthreads();
-  float* stage = reinterpret_cast<float*>(smem_kt) + w * 16 * (D + 4);
+  // Epilogue: stage the wave's 16 keys through LDS (d-major accumulators to key-major
+  // rows) and write dK = scale * acc, dV = acc with row stores.
+  float* stage = reinterpret_cast<float*>(smem) + w * 16 * (D + 4);
 #pragma unroll
-  for (int kt = 0; kt < KW; ++kt) {
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int r = 0; r < 4; ++r)
+        stage[lc * (D + 4) + 16 * dt + 4 * lg + r] = which == 0 ? adK[dt][r] * p.scale : adV[dt][r];
+    __syncthreads();
+    const int kl = lane >> 2;
+    const int key = kb + 16 * w + kl;
+    if (key < Tk) {
+      const int64_t* st = which == 0 ? p.sdk : p.sdv;
+      void* base = which == 0 ? p.dk : p.dv;
+      const int64_t o = (int64_t)b * st[0] + (int64_t)key * st[1] + (int64_t)kvh * st[2];
+      const float* src = stage + kl * (D + 4);
+      constexpr int PER = D / 4;
+      const int c0 = (lane & 3) * PER;
+      if (p.out_bf16) {
+        __bf16* dst = reinterpret_cast<__bf16*>(base) + o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          stage[lc * (D + 4) + 16 * dt + 4 * lg + r] = which == 0 ? adK[kt][dt][r] * p.scale : adV[kt][dt][r];
-      __syncthreads();
-      const int kl = lane >> 2;
-      const int key = kb + (w * KW + kt) * 16 + kl;
-      if (key < Tk) {
-        const int64_t* st = which == 0 ? p.sdk : p.sdv;
-        void* base = which == 0 ? p.dk : p.dv;
-        const int64_t o = (int64_t)b * st[0] + (int64_t)key * st[1] + (int64_t)kvh * st[2];
-        const float* src = stage + kl * (D + 4);
-        constexpr int PER = D / 4;
-        const int c0 = (lane & 3) * PER;
-        if (p.out_bf16) {
-          __bf16* dst = reinterpret_cast<__bf16*>(base) + o;
+        for (int c = 0; c < PER; c += 8) {
+          bf16x8 v;
 #pragma unroll
-          for (int c = 0; c < PER; c += 8) {
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[c0 + c + e];
-            *reinterpret_cast<bf16x8*>(dst + c0 + c) = v;
-          }
-        } else {
-          float* dst = reinterpret_cast<float*>(base) + o;
-#pragma unroll
-          for (int c = 0; c < PER; c += 4)
-            *reinterpret_cast<float4*>(dst + c0 + c) =
-                make_float4(src[c0 + c], src[c0 + c + 1], src[c0 + c + 2], src[c0 + c + 3]);
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[c0 + c + e];
+          *reinterpret_cast<bf16x8*>(dst + c0 + c) = v;
         }
+      } else {
+        float* dst = reinterpret_cast<float*>(base) + o;
+#pragma unroll
+        for (int c = 0; c < PER; c += 4)
+          *reinterpret_cast<float4*>(dst + c0 + c) = make_float4(src[c0 + c], src[c0 + c + 1], src[c0 + c + 2], src[c0 + c + 3]);
       }
-      __syncthreads();
     }
-  }
-}
-
-// ------------------------------------------------------------------------------ dQ final
-template <typename EO>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc, EO* __restrict__ dq,
-                                                          int B, int Tq, int Hq, int D, int64_t s0, int64_t s1,
-                                                          int64_t s2, float scale) {
-  const int64_t n4 = (int64_t)B * Tq * Hq * D / 4;
-  const int D4 = D / 4;
-  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n4; idx += (int64_t)gridDim.x * blockDim.x) {
-    const int c = idx % D4;
-    int64_t rest = idx / D4;
-    const int h = rest % Hq;
-    rest /= Hq;
-    const int t = rest % Tq;
-    const int b = rest / Tq;
-    const float4 a = reinterpret_cast<const float4*>(acc)[idx];
-    EO* dst = dq + b * s0 + t * s1 + h * s2 + 4 * c;
-    dst[0] = from_f32<EO>(a.x * scale);
-    dst[1] = from_f32<EO>(a.y * scale);
-    dst[2] = from_f32<EO>(a.z * scale);
-    dst[3] = from_f32<EO>(a.w * scale);
   }
 }
 
 template <typename E, int D>
-hipError_t pre_dispatch(const AttnParams& p, int mode, hipStream_t s) {
-  const dim3 grid((p.Tq + 127) / 128, p.Hq, p.B);
+hipError_t dq_dispatch(const AttnParams& p, int mode, hipStream_t s) {
+  const dim3 grid(p.B * p.Hq, (p.Tq + kWaves * 16 - 1) / (kWaves * 16));
   switch (mode) {
-    case PRE_LSE_GIVEN: hipLaunchKernelGGL((flash_pre_kernel<E, D, PRE_LSE_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
-    case PRE_LSE_COMPUTE: hipLaunchKernelGGL((flash_pre_kernel<E, D, PRE_LSE_COMPUTE>), grid, dim3(kThreads), 0, s, p); break;
-    case PRE_LSE_ONLY: hipLaunchKernelGGL((flash_pre_kernel<E, D, PRE_LSE_ONLY>), grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((flash_pre_kernel<E, D, PRE_P_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
+    case ROW_LSE_GIVEN: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
+    case ROW_LSE_COMPUTE: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_COMPUTE>), grid, dim3(kThreads), 0, s, p); break;
+    case ROW_LSE_ONLY: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_ONLY>), grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_P_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }
 
-template <typename E, int D, int KW>
-hipError_t main_dispatch(const AttnParams& p, hipStream_t s) {
-  constexpr int BN = kWaves * 16 * KW;
+template <typename E, int D>
+hipError_t dkdv_dispatch(const AttnParams& p, hipStream_t s) {
+  constexpr int BN = kWaves * 16;
   // x = (batch, kv-head) so that every head's heaviest (earliest) key block is issued first.
   const dim3 grid(p.B * p.Hkv, (p.Tk + BN - 1) / BN);
   if (p.P)
-    hipLaunchKernelGGL((flash_main_kernel<E, D, KW, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((flash_dkdv_kernel<E, D, true>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((flash_main_kernel<E, D, KW, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((flash_dkdv_kernel<E, D, false>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_flash_pre(const AttnParams& p, int mode, hipStream_t s) {
-  if (p.in_bf16) return p.D == 128 ? pre_dispatch<__bf16, 128>(p, mode, s) : pre_dispatch<__bf16, 64>(p, mode, s);
-  return p.D == 128 ? pre_dispatch<float, 128>(p, mode, s) : pre_dispatch<float, 64>(p, mode, s);
+hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s) {
+  if (p.in_bf16) return p.D == 128 ? dq_dispatch<__bf16, 128>(p, mode, s) : dq_dispatch<__bf16, 64>(p, mode, s);
+  return p.D == 128 ? dq_dispatch<float, 128>(p, mode, s) : dq_dispatch<float, 64>(p, mode, s);
 }
 
-hipError_t launch_flash_main(const AttnParams& p, hipStream_t s) {
-  if (p.in_bf16) return p.D == 128 ? main_dispatch<__bf16, 128, 2>(p, s) : main_dispatch<__bf16, 64, 2>(p, s);
-  return p.D == 128 ? main_dispatch<float, 128, 1>(p, s) : main_dispatch<float, 64, 1>(p, s);
-}
-
-hipError_t launch_dq_finalize(const AttnParams& p, hipStream_t s) {
-  const int64_t n4 = (int64_t)p.B * p.Tq * p.Hq * p.D / 4;
-  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
-  if (p.out_bf16)
-    hipLaunchKernelGGL((dq_finalize_kernel<__bf16>), dim3(blocks), dim3(256), 0, s, p.dq_acc,
-                       reinterpret_cast<__bf16*>(p.dq), p.B, p.Tq, p.Hq, p.D, p.sdq[0], p.sdq[1], p.sdq[2], p.scale);
-  else
-    hipLaunchKernelGGL((dq_finalize_kernel<float>), dim3(blocks), dim3(256), 0, s, p.dq_acc,
-                       reinterpret_cast<float*>(p.dq), p.B, p.Tq, p.Hq, p.D, p.sdq[0], p.sdq[1], p.sdq[2], p.scale);
-  return hipGetLastError();
+hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s) {
+  if (p.in_bf16) return p.D == 128 ? dkdv_dispatch<__bf16, 128>(p, s) : dkdv_dispatch<__bf16, 64>(p, s);
+  return p.D == 128 ? dkdv_dispatch<float, 128>(p, s) : dkdv_dispatch<float, 64>(p, s);
 }
 
 }  // namespace vtb

@@ -16,9 +16,8 @@ struct AttnParams {
   const void* dout;
   const float* lse;   // row log-sum-exp read by the backward (given or workspace)
   const float* P;     // saved softmax [B, Hq, Tq, Tk] or nullptr
-  float* lse_out;     // where a pre-pass that computes lse writes it
+  float* lse_out;     // where a pass that computes lse writes it
   float* dlt;         // workspace [B, Hq, Tq]: D_i = rowsum(P o dP)
-  float* dq_acc;      // workspace [B, Tq, Hq, D] fp32 dQ accumulator (unscaled)
   void* dq;
   void* dk;
   void* dv;
@@ -29,13 +28,14 @@ struct AttnParams {
   int64_t sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
 };
 
-enum PreMode { PRE_LSE_GIVEN = 0, PRE_LSE_COMPUTE = 1, PRE_LSE_ONLY = 2, PRE_P_GIVEN = 3 };
+// How the query-parallel pass obtains P: from the given lse, by computing lse itself
+// (online max/sum), lse only (no backward), or from a saved softmax P.
+enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3 };
 
-// Flash-style path (any Tq): pre-pass (row term D, optionally lse; zeroes dq_acc),
-// KV-parallel main pass (dK, dV written, dQ accumulated into dq_acc), dQ finalisation.
-hipError_t launch_flash_pre(const AttnParams& p, int mode, hipStream_t s);
-hipError_t launch_flash_main(const AttnParams& p, hipStream_t s);
-hipError_t launch_dq_finalize(const AttnParams& p, hipStream_t s);
+// Flash-style path (any Tq): query-parallel pass (row term D, lse when computed, dQ),
+// then key-parallel pass (dK, dV). The second reads D (and lse) written by the first.
+hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s);
+hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s);
 
 // Decode path (Hq/Hkv * Tq <= 16): split-KV chunk statistics, per-chunk gradients, dQ
 // reduction over chunks. Workspace layout is owned by attn_decode.hip.
