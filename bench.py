@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the attention-layer backward on one MI355X.
 
-One step = one attn_bwd call (row-term pre-pass, KV-parallel main pass, dQ finalisation)
-over the causal training workload B4 H20 T512 d128: q, k, v, dO bf16 ~ N(0, 1), saved
+One step = one attn_bwd call (query-parallel dq pass, key-parallel dk/dv pass) over the
+causal training workload B4 H20 T512 d128: q, k, v, dO bf16 ~ N(0, 1), saved
 row log-sum-exp fp32 (from the library's own attn_fwd_lse, computed before timing),
 scale 1/sqrt(128), bf16 outputs with fp32 accumulation. Inputs are resident in HBM
 before the timed region. By default the step rotates over 8 copies of inputs, outputs
@@ -11,8 +11,8 @@ a warm number (one set reused) is reported beside it.
 
 Prints ONE JSON line. `value` is TFLOP/s of the five contractions the method counts
 (S recompute, dP, dQ, dK, dV) on the exact causal triangle: 10 * d * B * H * T(T+1)/2.
-The roofline object is for the dominant kernel (the KV-parallel main pass), timed live
-with HIP events recorded by attn_bwd_timed on the launch stream.
+The roofline object is for the dominant kernel (the longer of the two passes), timed
+live with HIP events that attn_bwd_timed records on the launch stream.
 """
 
 from __future__ import annotations
@@ -32,7 +32,7 @@ METRIC = "attn-backward TFLOP/s & HBM GB/s at B4·H20·T512·d128; % of roofline
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MAIN_KERNEL_SRC = os.path.join(ROOT, "verified_transformer_backward_amd", "csrc", "attn_flash_bwd.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_main_causal_train_B4H20T512d128_pmc.json")
+PMC_SUMMARY = {k: os.path.join(ROOT, "profiles", f"attn_{k}_causal_train_B4H20T512d128_pmc.json") for k in ("dq", "dkdv")}
 
 
 def parse():
@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=8, help="rotating input/output sets (1 = warm only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-baseline sample time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (for scaling profiler byte counters)")
     return ap.parse_args()
 
 
@@ -85,21 +87,28 @@ class HipEvents:
 
 
 def workload_numbers(B, T, H, d):
+    """Algorithmic work of the step and of each pass (causal triangle, bf16 in/out).
+
+    dq pass:   S, dP, dQ contractions; reads q, k, v, dO, lse once, writes D and dQ.
+    dkdv pass: S, dP, dV, dK contractions; reads q, k, v, dO, lse, D once, writes dK, dV.
+    """
     pairs = B * H * T * (T + 1) // 2                      # visible (query, key) pairs
-    flops = 10 * d * pairs                                # 5 contractions x 2 d per pair
+    flops = 10 * d * pairs                                # the 5 contractions the method counts
     n = B * T * H * d
-    compulsory = 4 * n * 2 + B * H * T * 4 + 3 * n * 2    # q,k,v,dO + lse in, dq,dk,dv bf16 out
-    # main pass: reads q, k, v, dO, lse and the row term D once; writes dk, dv (bf16) and
-    # the fp32 dQ accumulator once
-    main_bytes = 4 * n * 2 + 2 * B * H * T * 4 + 2 * n * 2 + n * 4
-    return flops, compulsory, main_bytes
+    rows = B * H * T
+    compulsory = 4 * n * 2 + rows * 4 + 3 * n * 2         # q,k,v,dO + lse in, dq,dk,dv bf16 out
+    per_kernel = {
+        "dq": {"flops": 6 * d * pairs, "bytes": 4 * n * 2 + rows * 4 + rows * 4 + n * 2},
+        "dkdv": {"flops": 8 * d * pairs, "bytes": 4 * n * 2 + 2 * rows * 4 + 2 * n * 2},
+    }
+    return flops, compulsory, per_kernel
 
 
-def traffic_from_profile():
-    """HBM bytes per main-pass launch from the committed rocprofv3 counter summary, or None
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
     when it is missing or was taken on a different version of the kernel source."""
     try:
-        rec = json.load(open(PMC_SUMMARY))
+        rec = json.load(open(PMC_SUMMARY[kernel]))
         src = hashlib.sha256(open(MAIN_KERNEL_SRC, "rb").read()).hexdigest()
         if rec.get("source_sha256") != src:
             return None
@@ -124,7 +133,7 @@ def cpu_baseline(x, seconds):
     # bounded sample: whole (b, h) heads of the same workload, cycling, until ~`seconds` of work
     heads = [(b, h) for b in range(B) for h in range(H)]
     dt, done = 0.0, 0
-    while dt < seconds and done < 20 * len(heads):
+    while dt < seconds and done < 200 * len(heads):
         b, h = heads[done % len(heads)]
         one = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "dout")}
         lse = A.attention_lse(one["q"], one["k"], x["scale"], True)
@@ -158,7 +167,7 @@ def main():
     B, T, H, d = 4, 512, 20, 128
     x = synth.causal_inputs(B, T, H, d)
     sc = float(x["scale"])
-    flops, compulsory, main_bytes = workload_numbers(B, T, H, d)
+    flops, compulsory, per_kernel = workload_numbers(B, T, H, d)
 
     dev = torch.device("cuda:0")
     base = {n: torch.from_numpy(synth.bf16_bits(x[n])).view(torch.bfloat16).to(dev) for n in ("q", "k", "v", "dout")}
@@ -174,6 +183,13 @@ def main():
         t["ws"] = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
         sets.append(t)
     torch.cuda.synchronize()
+
+    if args.calibrate_copy:   # known-size reference for FETCH_SIZE / WRITE_SIZE: 256 MiB read + 256 MiB written
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     hip = HipEvents()
     stream = torch.cuda.current_stream()
@@ -193,12 +209,11 @@ def main():
         hip.record(stop, sptr)
         torch.cuda.synchronize()
         total = hip.ms(start, stop)
-        per = {k: [] for k in ("pre", "main", "final")}
+        per = {k: [] for k in ("dq", "dkdv")}
         for i in range(nsteps):
             e = phase[4 * i:4 * i + 4]
-            per["pre"].append(hip.ms(e[0], e[1]))
-            per["main"].append(hip.ms(e[1], e[2]))
-            per["final"].append(hip.ms(e[2], e[3]))
+            per["dq"].append(hip.ms(e[0], e[1]))
+            per["dkdv"].append(hip.ms(e[1], e[2]))
         hip.destroy(phase + [start, stop])
         return total / nsteps, {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
 
@@ -209,9 +224,10 @@ def main():
     warm_ms, warm_us = timed(max(10, args.steps // 2), 1)
 
     tflops = flops / (ms_step * 1e-3) / 1e12
-    main_s = kern_us["main"] * 1e-6
-    achieved = main_bytes / main_s / 1e9
-    traffic = traffic_from_profile()
+    dom = max(kern_us, key=kern_us.get)                   # dominant kernel of the step
+    dom_s = kern_us[dom] * 1e-6
+    achieved = per_kernel[dom]["bytes"] / dom_s / 1e9
+    traffic = traffic_from_profile(dom)
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -236,9 +252,11 @@ def main():
                  "kernel_us": {k: round(v, 2) for k, v in warm_us.items()}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "flash_main_kernel<bf16, 128, 2, false>",
-                     "algorithmic_bytes": main_bytes,
-                     "mfma_tflops": round(flops / main_s / 1e12, 1)},
+                     "kernel": f"flash_{dom}_kernel (bf16, d128)",
+                     "algorithmic_bytes": per_kernel[dom]["bytes"],
+                     "algorithmic_flops": per_kernel[dom]["flops"],
+                     "mfma_tflops": round(per_kernel[dom]["flops"] / dom_s / 1e12, 1),
+                     "mfma_frac": round(per_kernel[dom]["flops"] / dom_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
