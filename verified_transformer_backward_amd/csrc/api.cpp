@@ -241,9 +241,16 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
     p.lse = p.lse_out;
     mode = vtb::ROW_LSE_COMPUTE;
   }
-  rc = hip_status(vtb::launch_flash_dq(p, mode, s), "flash dq pass");
+  const bool mfma = vtb::mfma_path_applicable(p);
+  if (mfma && mode == vtb::ROW_LSE_GIVEN)
+    rc = hip_status(vtb::launch_mfma_dq(p, s), "dq pass");
+  else
+    rc = hip_status(vtb::launch_flash_dq(p, mode, s), "flash dq pass");
   if (rc || (rc = ev.mark(s))) return rc;
-  rc = hip_status(vtb::launch_flash_dkdv(p, s), "flash dk/dv pass");
+  if (mfma && !P)
+    rc = hip_status(vtb::launch_mfma_dkdv(p, s), "dk/dv pass");
+  else
+    rc = hip_status(vtb::launch_flash_dkdv(p, s), "flash dk/dv pass");
   if (rc || (rc = ev.mark(s))) return rc;
   return ev.mark(s);   // two launches on this path: the last two events coincide
 }

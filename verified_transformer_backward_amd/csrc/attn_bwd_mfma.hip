@@ -1,0 +1,606 @@
+// Attention backward for bf16 inputs with head dim 128: MFMA tiles fed by direct-to-LDS
+// loads, double-buffered, one barrier per block.
+//
+// Same chain as attn_flash_bwd.hip ("Hesper.Training.VerifiedBackward", section
+// "Attention (full single-head)", with the causal mask of the DaisyChain-Train
+// transformer.js `backward`), laid out for gfx950's matrix cores:
+//
+//   dq    query-parallel, ONE sweep over the visible keys. With P = exp(S - lse) known
+//         from the saved lse, dS = P o (dP - D) gives
+//             dQ = scale (sum_j (P o dP)_ij k_j  -  D_i sum_j P_ij k_j),
+//         so the sweep accumulates A = (P o dP) K, B = P K and D = rowsum(P o dP)
+//         together and forms dQ = scale (A - D B) at the end: four contractions per
+//         key block instead of two sweeps of five. Writes dQ and D.
+//   dkdv  key-parallel over query blocks (of every q-head of the kv-head's group):
+//         S, dP, then dV += P^T dO and dK += dS^T Q with dS = P o (dP - D), D from dq.
+//
+// A wave owns NT 16-row MFMA tiles of queries (dq) or keys (dkdv); every operand
+// fragment it reads from LDS feeds NT MFMAs. K/V (dq) and Q/dO (dkdv) blocks of 64 rows
+// are double buffered: the direct-to-LDS loads of the next block run under the current
+// block's MFMAs, and one barrier per block both publishes the new block and retires the
+// old one. Rows past the end of a tensor re-read its last row, so values stay finite and
+// every use of them is masked; no load needs a bounds branch. Blocks that need no mask
+// run a branch-free body. The LDS layout is the swizzled one of lds_tile.h, free of bank
+// conflicts for the row reads, the transpose reads and the direct-to-LDS writes.
+#include "device_common.h"
+#include "launch.h"
+#include "lds_tile.h"
+
+#include <type_traits>
+
+namespace vtb {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kHD = 128;        // head dim
+constexpr int kNKS = kHD / 32;  // 32-deep k steps over the head dim
+constexpr int kNDT = kHD / 16;  // 16-wide tiles over the head dim
+constexpr int kRows = 64;       // rows per staged block
+using LT = Lds<__bf16, kHD>;
+
+#ifndef VTB_MFMA_TILES          // 16-row MFMA tiles per wave
+#define VTB_MFMA_TILES 1
+#endif
+#ifndef VTB_MFMA_WAVES          // waves per workgroup
+#define VTB_MFMA_WAVES 4
+#endif
+constexpr int kNT = VTB_MFMA_TILES;
+constexpr int kW = VTB_MFMA_WAVES;
+constexpr int kT = 64 * kW;
+constexpr int kWavesPerEU = kNT == 1 ? 2 : 1;   // register budget: 256 or 512 per lane
+#ifndef VTB_MFMA_BUFS           // staged blocks in flight: loads run NBUF - 1 blocks ahead
+#define VTB_MFMA_BUFS 2
+#endif
+constexpr int kBufs = VTB_MFMA_BUFS;
+static_assert(kW == 4 || kW == 8, "64-row tiles are staged four rows per load by every wave");
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// s_waitcnt vmcnt(0): every vector-memory load of the wave, the direct-to-LDS ones
+// included, has landed. A real waitcnt instruction, so the compiler also knows that its
+// own earlier loads are complete and adds no waits for them inside the block loops.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt vmcnt(n): at most n vector-memory loads of the wave still in flight. Loads
+// complete in issue order, so this waits for everything but the n youngest.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm_upto(int n) {   // n is wave-uniform
+  switch (n) {
+#define VTB_WAIT_CASE(k) case k: wait_vm<k>(); break;
+    VTB_WAIT_CASE(1) VTB_WAIT_CASE(2) VTB_WAIT_CASE(3) VTB_WAIT_CASE(4) VTB_WAIT_CASE(5) VTB_WAIT_CASE(6)
+    VTB_WAIT_CASE(7) VTB_WAIT_CASE(8) VTB_WAIT_CASE(9) VTB_WAIT_CASE(10) VTB_WAIT_CASE(11) VTB_WAIT_CASE(12)
+    VTB_WAIT_CASE(13) VTB_WAIT_CASE(14) VTB_WAIT_CASE(15) VTB_WAIT_CASE(16) VTB_WAIT_CASE(17) VTB_WAIT_CASE(18)
+    VTB_WAIT_CASE(19) VTB_WAIT_CASE(20) VTB_WAIT_CASE(21) VTB_WAIT_CASE(22) VTB_WAIT_CASE(23) VTB_WAIT_CASE(24)
+#undef VTB_WAIT_CASE
+    default: wait_loads(); break;
+  }
+}
+
+// Scheduling fence: keeps the issue order of the operand-read groups written around it,
+// so LDS reads run ahead of the MFMAs that consume them.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Direct-to-LDS loads, issued through inline assembly. Each lane reads `bytes` bytes at
+// sbase + voff (sbase wave-uniform) and writes them to LDS at m0 + lane * bytes. Written
+// as assembly so that the compiler does not treat the asynchronous LDS write as aliasing
+// every later LDS read (it would then wait for the load before each block's reads); the
+// order is kept explicitly instead: wait_loads() + __syncthreads() before any read of a
+// staged buffer, and a buffer is refilled only after the barrier that retires it. The
+// s_nop covers the one wait state gfx9 needs between writing M0 and an LDS DMA.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// Direct-to-LDS staging of 64 rows of one head into a swizzled 64 x 128 tile. Wave w
+// writes rows RPW w .. RPW w + RPW - 1, four rows (1 KB) per load: lane l lands at
+// physical chunk l % 16 of row 4i + l / 16 and so fetches the logical chunk the swizzle
+// keeps there. The lane part of the source offset only depends on the parity of i.
+struct RowStager {
+  static constexpr int RPW = kRows / kW;
+  static constexpr int NI = RPW / 4;
+  int loff[2];   // lane offsets (elements) for even / odd i
+  int w;
+  __device__ __forceinline__ void init(int wave, int64_t tstride) {
+    w = wave;
+    const int lane = threadIdx.x & 63, sub = lane >> 4, pc = lane & 15;
+    const int hbit = ((RPW * w) >> 4) & 1;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      loff[par] = sub * (int)tstride + 8 * (pc ^ ((((4 * par + sub) & 7) << 1) | hbit));
+  }
+  // Load i (0 .. NI-1) of rows [t0, t0 + 64) of `head` (row t at head + t * tstride);
+  // rows >= tlimit read row tlimit - 1.
+  __device__ __forceinline__ void stage_one(__bf16* tile, const __bf16* head, int64_t tstride, int t0, int tlimit,
+                                            int i) const {
+    if (t0 + kRows <= tlimit) {
+      const __bf16* rowp = head + (int64_t)(t0 + RPW * w + 4 * i) * tstride;
+      dma16(rowp, 2u * (uint32_t)loff[i & 1], lds_addr(tile + (RPW * w + 4 * i) * kHD));
+    } else {
+      const int lane = threadIdx.x & 63;
+      const int row = RPW * w + 4 * i + (lane >> 4);
+      const int t = min(t0 + row, tlimit - 1) - t0;   // 0 .. 63
+      const uint32_t voff = 2u * (uint32_t)(t * (int)tstride + 8 * ((lane & 15) ^ LT::chunk_xor(row)));
+      dma16(head + (int64_t)t0 * tstride, voff, lds_addr(tile + (RPW * w + 4 * i) * kHD));
+    }
+  }
+  __device__ __forceinline__ void stage(__bf16* tile, const __bf16* head, int64_t tstride, int t0, int tlimit) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) stage_one(tile, head, tstride, t0, tlimit, i);
+  }
+};
+
+// 64 consecutive fp32 values src[i0 .. i0 + 63] (indices clamped to n - 1) into LDS, one
+// direct-to-LDS dword per lane; called by a single wave.
+__device__ __forceinline__ void stage_vals64(float* dst, const float* src, int i0, int n) {
+  const int lane = threadIdx.x & 63;
+  dma4(src + i0, 4u * (uint32_t)(min(i0 + lane, n - 1) - i0), lds_addr(dst));
+}
+
+// Four consecutive output elements (fp32 or bf16 RNE).
+__device__ __forceinline__ void store4(void* base, int bf16, int64_t off, float a, float b, float c, float d) {
+  if (bf16) {
+    bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base) + off) = v;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(a, b, c, d);
+  }
+}
+
+// ------------------------------------------------------------------------------ dq
+// Workgroup: kW * 16 * kNT query rows of one q-head; wave w owns kNT 16-row tiles
+// starting at qw0. Per 64-key block the wave computes S^T = K Q^T and dP^T = V dO^T
+// (keys as MFMA rows, so a lane owns one query column and its row sums stay in the
+// lane), then A^T += K^T (P o dP)^T and B^T += K^T P^T with K^T from LDS transpose reads.
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
+void dq_mfma_kernel(AttnParams p) {
+  constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[kBufs][2][BN * kHD];   // [buffer][K, V]
+
+  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const int nqb = (p.Tq + BM - 1) / BM;
+  const int qb = nqb - 1 - (int)blockIdx.y;   // causal: heaviest query block first
+  const int G = p.Hq / p.Hkv, kvh = h / G;
+  const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
+  const float sl2 = p.scale * kLog2e;
+  const int64_t rowbase = ((int64_t)b * p.Hq + h) * Tq;
+  const int qw0 = qb * BM + QW * w;
+
+  const __bf16* Qh = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)h * p.sq[2];
+  const __bf16* Oh = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.sdo[0] + (int64_t)h * p.sdo[2];
+  const __bf16* Kh = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.sk[0] + (int64_t)kvh * p.sk[2];
+  const __bf16* Vh = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.sv[0] + (int64_t)kvh * p.sv[2];
+
+  // Q and dO of the lane's queries: B operands (k = d, n = query) of S^T and dP^T.
+  bf16x8 qa[kNT][kNKS], da[kNT][kNKS];
+  float lse2[kNT];
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    const int i = min(qw0 + 16 * qt + lc, Tq - 1);
+#pragma unroll
+    for (int ks = 0; ks < kNKS; ++ks) {
+      qa[qt][ks] = load8<__bf16>(Qh + (int64_t)i * p.sq[1] + 32 * ks + 8 * lg);
+      da[qt][ks] = load8<__bf16>(Oh + (int64_t)i * p.sdo[1] + 32 * ks + 8 * lg);
+    }
+    lse2[qt] = p.lse[rowbase + i] * kLog2e;
+  }
+
+  f32x4 acA[kNDT][kNT], acB[kNDT][kNT];
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < kNT; ++qt) {
+      acA[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acB[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float dsum[kNT];
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) dsum[qt] = 0.f;
+
+  const int last_row = min(Tq, (qb + 1) * BM) - 1;
+  const int kend = p.causal ? min(Tk, last_row + off + 1) : Tk;
+  const int nblk = (kend + BN - 1) / BN;
+  // keys this wave needs: none when its rows start past Tq
+  const int wkend = qw0 >= Tq ? 0 : (p.causal ? min(Tk, min(Tq - 1, qw0 + QW - 1) + off + 1) : Tk);
+
+  RowStager kst, vst;
+  kst.init(w, p.sk[1]);
+  vst.init(w, p.sv[1]);
+  constexpr int DMA_PER_BLOCK = 2 * RowStager::NI;   // direct-to-LDS loads per wave per block
+  // The register loads above complete before any direct-to-LDS load is issued, so the
+  // compiler needs no waits for them inside the loop (it does not see the LDS loads).
+  wait_loads();
+#pragma unroll
+  for (int s = 0; s < kBufs - 1; ++s)
+    if (s < nblk) {
+      kst.stage(sm[s][0], Kh, p.sk[1], s * BN, Tk);
+      vst.stage(sm[s][1], Vh, p.sv[1], s * BN, Tk);
+    }
+  int cur = 0;   // buffer of block j
+
+  auto block = [&](const __bf16* sK, const __bf16* sV, int jb, auto full_tag, auto&& dma) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // S^T, dP^T: tile kt holds keys jb + 16 kt + 4 lg + r (reg r) for query column lc.
+    // The K and V row fragments of tile kt + 1 are read while tile kt's MFMAs run.
+    f32x4 sT[4][kNT], dT[4][kNT];
+    bf16x8 fk[2][kNKS], fv[2][kNKS];
+    auto read_rows = [&](int kt, bf16x8(&ak)[kNKS], bf16x8(&av)[kNKS]) {
+#pragma unroll
+      for (int ks = 0; ks < kNKS; ++ks) {
+        ak[ks] = row8<LT>(sK, 16 * kt + lc, 32 * ks + 8 * lg);
+        av[ks] = row8<LT>(sV, 16 * kt + lc, 32 * ks + 8 * lg);
+      }
+    };
+    read_rows(0, fk[0], fv[0]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (kt + 1 < 4) read_rows(kt + 1, fk[(kt + 1) & 1], fv[(kt + 1) & 1]);
+      if (kt == 0 || kt == 2) dma(kt >> 1);
+      fence();
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt) {
+        sT[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dT[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kNKS; ++ks) {
+          mma(sT[kt][qt], fk[kt & 1][ks], qa[qt][ks]);
+          mma(dT[kt][qt], fv[kt & 1][ks], da[qt][ks]);
+        }
+      }
+      fence();
+    }
+    // K^T fragments of the first (dt, c) pairs are read under the softmax arithmetic.
+    constexpr int NP = kNDT * 2, AHEAD = 4;
+    bf16x8 kT[AHEAD + 1];
+    auto read_kT = [&](int pr) { return col8<LT>(sK, 32 * (pr & 1) + 4 * lg, 32 * (pr & 1) + 16 + 4 * lg, 16 * (pr >> 1)); };
+#pragma unroll
+    for (int pr = 0; pr < AHEAD; ++pr) kT[pr] = read_kT(pr);
+    fence();
+    // P and P o dP as bf16 B operands (k = 32 keys, n = query): element e of operand c
+    // is key 32c + 4 lg + e (e < 4) or 32c + 16 + 4 lg + e - 4 (e >= 4).
+    bf16x8 pb[2][kNT], xb[2][kNT];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pr = __builtin_amdgcn_exp2f(sT[kt][qt][r] * sl2 - lse2[qt]);
+          if constexpr (!FULL) {
+            const int jj = jb + 16 * kt + 4 * lg + r, i = qw0 + 16 * qt + lc;
+            pr = ((jj < Tk) & (!p.causal | (jj <= i + off))) ? pr : 0.f;
+          }
+          const float x = pr * dT[kt][qt][r];
+          dsum[qt] += x;
+          pb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)pr;
+          xb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)x;
+        }
+    fence();
+    // A^T += K^T (P o dP)^T,  B^T += K^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (pr + AHEAD < NP) kT[(pr + AHEAD) % (AHEAD + 1)] = read_kT(pr + AHEAD);
+      if (pr == 0 || pr == NP / 2) dma(2 + (pr != 0));
+      fence();
+      const int dt = pr >> 1, c = pr & 1;
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt) {
+        mma(acA[dt][qt], kT[pr % (AHEAD + 1)], xb[c][qt]);
+        mma(acB[dt][qt], kT[pr % (AHEAD + 1)], pb[c][qt]);
+      }
+      fence();
+    }
+  };
+
+  for (int j = 0; j < nblk; ++j) {
+    const int jb = j * BN;
+    // blocks j + 1 .. j + kBufs - 2 (those issued) may stay in flight
+    wait_vm_upto(DMA_PER_BLOCK * (min(nblk - 1, j + kBufs - 2) - j));
+    __syncthreads();   // block j is in LDS; every wave is done with block j - 1
+    // The loads of block j + kBufs - 1 go to the buffer block j - 1 just freed; they are
+    // issued right after the barrier, ahead of this block's MFMAs.
+    const int nxt = cur == 0 ? kBufs - 1 : cur - 1;
+    const bool more = j + kBufs - 1 < nblk;
+    const int tn = jb + (kBufs - 1) * BN;
+    auto dma = [&](int part) {
+      if (!more || part != 0) return;
+      kst.stage(sm[nxt][0], Kh, p.sk[1], tn, Tk);
+      vst.stage(sm[nxt][1], Vh, p.sv[1], tn, Tk);
+    };
+    const int bj = cur;
+    cur = cur + 1 == kBufs ? 0 : cur + 1;
+    if (jb >= wkend) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) dma(part);
+      continue;
+    }
+    const bool full = jb + BN <= Tk && (!p.causal || jb + BN - 1 <= qw0 + off);
+    if (full)
+      block(sm[bj][0], sm[bj][1], jb, std::true_type{}, dma);
+    else
+      block(sm[bj][0], sm[bj][1], jb, std::false_type{}, dma);
+  }
+
+  // D of the lane's queries: the four 16-lane groups hold disjoint key subsets.
+  float Dq[kNT];
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    float d = dsum[qt];
+    d += __shfl_xor(d, 16, 64);
+    d += __shfl_xor(d, 32, 64);
+    Dq[qt] = d;
+    const int i = qw0 + 16 * qt + lc;
+    if (lg == 0 && i < Tq) p.dlt[rowbase + i] = d;
+  }
+  // dQ = scale (A - D B): the lane holds d = 16 dt + 4 lg + r of query qw0 + 16 qt + lc.
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    const int i = qw0 + 16 * qt + lc;
+    if (i < Tq) {
+      const int64_t o = (int64_t)b * p.sdq[0] + (int64_t)i * p.sdq[1] + (int64_t)h * p.sdq[2] + 4 * lg;
+#pragma unroll
+      for (int dt = 0; dt < kNDT; ++dt) {
+        const f32x4 a = acA[dt][qt], bb = acB[dt][qt];
+        const float s = p.scale, dd = Dq[qt];
+        store4(p.dq, p.out_bf16, o + 16 * dt, s * (a[0] - dd * bb[0]), s * (a[1] - dd * bb[1]), s * (a[2] - dd * bb[2]),
+               s * (a[3] - dd * bb[3]));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ dkdv
+// Workgroup: kW * 16 * kNT keys of one kv-head; wave w owns kNT 16-key tiles starting
+// at kw0, K and V in registers as B operands. For every (q-head of the group, 64-query
+// block) that sees the keys: S = Q K^T, dP = dO V^T (queries as MFMA rows), P and dS
+// with the block's lse and D, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
+// from LDS transpose reads. dK and dV are written once, in a fixed head order.
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
+void dkdv_mfma_kernel(AttnParams p) {
+  constexpr int BM = kRows, KW = 16 * kNT, BN = kW * KW;
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[kBufs][2][BM * kHD];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float sv[kBufs][2][BM];            // [buffer][lse, D]
+
+  const int b = blockIdx.x / p.Hkv, kvh = blockIdx.x % p.Hkv;
+  const int kb = blockIdx.y * BN;
+  const int G = p.Hq / p.Hkv;
+  const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
+  const float sl2 = p.scale * kLog2e;
+  const int kw0 = kb + KW * w;
+
+  const __bf16* Kh = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.sk[0] + (int64_t)kvh * p.sk[2];
+  const __bf16* Vh = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.sv[0] + (int64_t)kvh * p.sv[2];
+  bf16x8 kr[kNT][kNKS], vr[kNT][kNKS];   // B operands (k = d, n = key kw0 + 16 kt + lc)
+#pragma unroll
+  for (int kt = 0; kt < kNT; ++kt) {
+    const int jj = min(kw0 + 16 * kt + lc, Tk - 1);
+#pragma unroll
+    for (int ks = 0; ks < kNKS; ++ks) {
+      kr[kt][ks] = load8<__bf16>(Kh + (int64_t)jj * p.sk[1] + 32 * ks + 8 * lg);
+      vr[kt][ks] = load8<__bf16>(Vh + (int64_t)jj * p.sv[1] + 32 * ks + 8 * lg);
+    }
+  }
+  f32x4 adK[kNDT][kNT], adV[kNDT][kNT];
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) {
+      adK[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      adV[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int q_first = p.causal ? max(0, kb - off) : 0;
+  const int qb0 = q_first / BM;
+  const int nqb = (Tq + BM - 1) / BM - qb0;
+  const int n_it = nqb > 0 ? G * nqb : 0;
+  const int wq_first = p.causal ? kw0 - off : 0;   // earlier queries see none of the wave's keys
+
+  RowStager qst, ost;
+  qst.init(w, p.sq[1]);
+  ost.init(w, p.sdo[1]);
+  auto stage = [&](int buf, int hh, int q0) {
+    const __bf16* Qh = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)hh * p.sq[2];
+    const __bf16* Oh = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.sdo[0] + (int64_t)hh * p.sdo[2];
+    qst.stage(sm[buf][0], Qh, p.sq[1], q0, Tq);
+    ost.stage(sm[buf][1], Oh, p.sdo[1], q0, Tq);
+    const int64_t rb = ((int64_t)b * p.Hq + hh) * Tq;
+    if (w == 0) stage_vals64(sv[buf][0], p.lse + rb, q0, Tq);
+    if (w == 1) stage_vals64(sv[buf][1], p.dlt + rb, q0, Tq);
+  };
+
+  auto block = [&](int buf, int q0, auto full_tag, auto&& dma) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const __bf16* sQ = sm[buf][0];
+    const __bf16* sO = sm[buf][1];
+    const f32x4* sL4 = reinterpret_cast<const f32x4*>(&sv[buf][0][0]);
+    const f32x4* sD4 = reinterpret_cast<const f32x4*>(&sv[buf][1][0]);
+    // S, dP: tile (qt, kt) reg r holds query q0 + 16 qt + 4 lg + r, key kw0 + 16 kt + lc.
+    // The Q and dO row fragments of tile qt + 1 are read while tile qt's MFMAs run.
+    f32x4 S[4][kNT], dP[4][kNT];
+    bf16x8 fq[2][kNKS], fo[2][kNKS];
+    auto read_rows = [&](int qt, bf16x8(&aq)[kNKS], bf16x8(&ao)[kNKS]) {
+#pragma unroll
+      for (int ks = 0; ks < kNKS; ++ks) {
+        aq[ks] = row8<LT>(sQ, 16 * qt + lc, 32 * ks + 8 * lg);
+        ao[ks] = row8<LT>(sO, 16 * qt + lc, 32 * ks + 8 * lg);
+      }
+    };
+    read_rows(0, fq[0], fo[0]);
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      if (qt + 1 < 4) read_rows(qt + 1, fq[(qt + 1) & 1], fo[(qt + 1) & 1]);
+      if (qt == 0 || qt == 2) dma(qt >> 1);
+      fence();
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) {
+        S[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dP[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kNKS; ++ks) {
+          mma(S[qt][kt], fq[qt & 1][ks], kr[kt][ks]);
+          mma(dP[qt][kt], fo[qt & 1][ks], vr[kt][ks]);
+        }
+      }
+      fence();
+    }
+    // dO^T and Q^T fragments of the first (dt, c) pairs are read under the arithmetic.
+    constexpr int NP = kNDT * 2, AHEAD = 3;
+    bf16x8 oT[AHEAD + 1], qT[AHEAD + 1];
+    auto read_T = [&](int pr, bf16x8& o, bf16x8& q) {
+      const int c = pr & 1, dt = pr >> 1;
+      o = col8<LT>(sO, 32 * c + 4 * lg, 32 * c + 16 + 4 * lg, 16 * dt);
+      q = col8<LT>(sQ, 32 * c + 4 * lg, 32 * c + 16 + 4 * lg, 16 * dt);
+    };
+    f32x4 Lv[4], Dv[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      Lv[qt] = sL4[4 * qt + lg];
+      Dv[qt] = sD4[4 * qt + lg];
+    }
+#pragma unroll
+    for (int pr = 0; pr < AHEAD; ++pr) read_T(pr, oT[pr], qT[pr]);
+    fence();
+    // P and dS as bf16 B operands (k = 32 queries, n = key): element e of operand c is
+    // query 32c + 4 lg + e (e < 4) or 32c + 16 + 4 lg + e - 4 (e >= 4).
+    bf16x8 pb[2][kNT], sb[2][kNT];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pr = __builtin_amdgcn_exp2f(S[qt][kt][r] * sl2 - Lv[qt][r] * kLog2e);
+          if constexpr (!FULL) {
+            const int i = q0 + 16 * qt + 4 * lg + r, jj = kw0 + 16 * kt + lc;
+            pr = ((i < Tq) & (jj < Tk) & (!p.causal | (jj <= i + off))) ? pr : 0.f;
+          }
+          pb[qt >> 1][kt][4 * (qt & 1) + r] = (__bf16)pr;
+          sb[qt >> 1][kt][4 * (qt & 1) + r] = (__bf16)(pr * (dP[qt][kt][r] - Dv[qt][r]));
+        }
+    }
+    fence();
+    // dV^T += dO^T P,  dK^T += Q^T dS over (dt, c) pairs (scale applied at the end)
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (pr + AHEAD < NP) read_T(pr + AHEAD, oT[(pr + AHEAD) % (AHEAD + 1)], qT[(pr + AHEAD) % (AHEAD + 1)]);
+      if (pr == 0 || pr == NP / 2) dma(2 + (pr != 0));
+      fence();
+      const int dt = pr >> 1, c = pr & 1;
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) {
+        mma(adV[dt][kt], oT[pr % (AHEAD + 1)], pb[c][kt]);
+        mma(adK[dt][kt], qT[pr % (AHEAD + 1)], sb[c][kt]);
+      }
+      fence();
+    }
+  };
+
+  // (head, query block) of the current and the next iteration, advanced without division
+  int h = kvh * G, q0 = qb0 * BM;
+  // iterations are prefetched kBufs - 1 ahead; (hs, q0s) walks the staged sequence. The
+  // register loads above complete first: the compiler then needs no waits for them in the
+  // loop (it does not see the direct-to-LDS loads).
+  wait_loads();
+  const int dma_per_it = 2 * RowStager::NI + (w < 2 ? 1 : 0);   // direct-to-LDS loads per wave
+  int hs = h, q0s = q0;
+#pragma unroll
+  for (int s = 0; s < kBufs - 1; ++s)
+    if (s < n_it) {
+      stage(s, hs, q0s);
+      q0s += BM;
+      if (q0s >= Tq) {
+        q0s = qb0 * BM;
+        ++hs;
+      }
+    }
+  int cur = 0;
+  for (int it = 0; it < n_it; ++it) {
+    wait_vm_upto(dma_per_it * (min(n_it - 1, it + kBufs - 2) - it));
+    __syncthreads();   // block `it` is in LDS; every wave is done with block it - 1
+    // The loads of iteration it + kBufs - 1 go to the buffer iteration it - 1 just freed,
+    // issued right after the barrier, ahead of this iteration's MFMAs.
+    const int nxt = cur == 0 ? kBufs - 1 : cur - 1;
+    const bool more = it + kBufs - 1 < n_it;
+    const __bf16* Qn = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)hs * p.sq[2];
+    const __bf16* On = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.sdo[0] + (int64_t)hs * p.sdo[2];
+    const int qn = q0s;
+    auto dma = [&](int part) {
+      if (!more || part != 0) return;
+      const int64_t rb = ((int64_t)b * p.Hq + hs) * Tq;
+      if (w == 0) stage_vals64(sv[nxt][0], p.lse + rb, qn, Tq);
+      if (w == 1) stage_vals64(sv[nxt][1], p.dlt + rb, qn, Tq);
+      qst.stage(sm[nxt][0], Qn, p.sq[1], qn, Tq);
+      ost.stage(sm[nxt][1], On, p.sdo[1], qn, Tq);
+    };
+    const int buf = cur;
+    cur = cur + 1 == kBufs ? 0 : cur + 1;
+    if (q0 + BM - 1 >= wq_first && kw0 < Tk) {
+      const bool full = q0 + BM <= Tq && kw0 + KW <= Tk && (!p.causal || kw0 + KW - 1 <= q0 + off);
+      if (full)
+        block(buf, q0, std::true_type{}, dma);
+      else
+        block(buf, q0, std::false_type{}, dma);
+    } else {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) dma(part);
+    }
+    if (more) {
+      q0s += BM;
+      if (q0s >= Tq) {
+        q0s = qb0 * BM;
+        ++hs;
+      }
+    }
+    q0 += BM;
+    if (q0 >= Tq) q0 = qb0 * BM;
+  }
+
+  // dK = scale acc, dV = acc: the lane holds d = 16 dt + 4 lg + r of key kw0 + 16 kt + lc.
+#pragma unroll
+  for (int kt = 0; kt < kNT; ++kt) {
+    const int jj = kw0 + 16 * kt + lc;
+    if (jj < Tk) {
+      const int64_t ok = (int64_t)b * p.sdk[0] + (int64_t)jj * p.sdk[1] + (int64_t)kvh * p.sdk[2] + 4 * lg;
+      const int64_t ov = (int64_t)b * p.sdv[0] + (int64_t)jj * p.sdv[1] + (int64_t)kvh * p.sdv[2] + 4 * lg;
+#pragma unroll
+      for (int dt = 0; dt < kNDT; ++dt) {
+        const f32x4 k4 = adK[dt][kt], v4 = adV[dt][kt];
+        const float s = p.scale;
+        store4(p.dk, p.out_bf16, ok + 16 * dt, s * k4[0], s * k4[1], s * k4[2], s * k4[3]);
+        store4(p.dv, p.out_bf16, ov + 16 * dt, v4[0], v4[1], v4[2], v4[3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool mfma_path_applicable(const AttnParams& p) { return p.in_bf16 && p.D == kHD; }
+
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s) {
+  constexpr int BM = kW * 16 * kNT;
+  const dim3 grid(p.B * p.Hq, (p.Tq + BM - 1) / BM);
+  hipLaunchKernelGGL(dq_mfma_kernel, grid, dim3(kT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s) {
+  constexpr int BN = kW * 16 * kNT;
+  const dim3 grid(p.B * p.Hkv, (p.Tk + BN - 1) / BN);
+  hipLaunchKernelGGL(dkdv_mfma_kernel, grid, dim3(kT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace vtb

@@ -37,6 +37,13 @@ enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_G
 hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s);
 hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s);
 
+// bf16, head dim 128: one wave per SIMD with 32-row MFMA blocks and direct-to-LDS tile
+// loads. The dq pass takes a given lse (single sweep; writes dQ and D); the dk/dv pass
+// takes lse and D from the workspace or the caller, like launch_flash_dkdv.
+bool mfma_path_applicable(const AttnParams& p);
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s);
+hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s);
+
 // Decode path (Hq/Hkv * Tq <= 16): split-KV chunk statistics, per-chunk gradients, dQ
 // reduction over chunks. Workspace layout is owned by attn_decode.hip.
 size_t decode_workspace_bytes(const AttnParams& p);
