@@ -9,10 +9,15 @@ before the timed region. By default the step rotates over 8 copies of inputs, ou
 and workspace (~760 MB) so no step finds its data in the 256 MB Infinity Cache ("cold");
 a warm number (one set reused) is reported beside it.
 
+The K timed steps are captured once into a HIP graph (the same two launches per step)
+and replayed between two HIP events, so the host's launch cost is not in the step time;
+the graph's outputs are checked bit for bit against an eager call before timing.
+
 Prints ONE JSON line. `value` is TFLOP/s of the five contractions the method counts
 (S recompute, dP, dQ, dK, dV) on the exact causal triangle: 10 * d * B * H * T(T+1)/2.
 The roofline object is for the dominant kernel (the longer of the two passes), timed
-live with HIP events that attn_bwd_timed records on the launch stream.
+live with HIP events that attn_bwd_timed records between the launches of eager steps on
+the launch stream (so a pass's time includes the dispatch gap before it).
 """
 
 from __future__ import annotations
@@ -31,7 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn-backward TFLOP/s & HBM GB/s at B4·H20·T512·d128; % of roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-MAIN_KERNEL_SRC = os.path.join(ROOT, "verified_transformer_backward_amd", "csrc", "attn_flash_bwd.hip")
+MAIN_KERNEL_SRC = os.path.join(ROOT, "verified_transformer_backward_amd", "csrc", "attn_bwd_mfma.hip")
 PMC_SUMMARY = {k: os.path.join(ROOT, "profiles", f"attn_{k}_causal_train_B4H20T512d128_pmc.json") for k in ("dq", "dkdv")}
 
 
@@ -89,8 +94,9 @@ class HipEvents:
 def workload_numbers(B, T, H, d):
     """Algorithmic work of the step and of each pass (causal triangle, bf16 in/out).
 
-    dq pass:   S, dP, dQ contractions; reads q, k, v, dO, lse once, writes D and dQ.
+    dq pass:   S, dP, (P o dP) K, P K contractions; reads q, k, v, dO, lse once, writes D, dQ.
     dkdv pass: S, dP, dV, dK contractions; reads q, k, v, dO, lse, D once, writes dK, dV.
+    Per-pass flops are the contractions the pass executes on the causal triangle.
     """
     pairs = B * H * T * (T + 1) // 2                      # visible (query, key) pairs
     flops = 10 * d * pairs                                # the 5 contractions the method counts
@@ -98,7 +104,7 @@ def workload_numbers(B, T, H, d):
     rows = B * H * T
     compulsory = 4 * n * 2 + rows * 4 + 3 * n * 2         # q,k,v,dO + lse in, dq,dk,dv bf16 out
     per_kernel = {
-        "dq": {"flops": 6 * d * pairs, "bytes": 4 * n * 2 + rows * 4 + rows * 4 + n * 2},
+        "dq": {"flops": 8 * d * pairs, "bytes": 4 * n * 2 + rows * 4 + rows * 4 + n * 2},
         "dkdv": {"flops": 8 * d * pairs, "bytes": 4 * n * 2 + 2 * rows * 4 + 2 * n * 2},
     }
     return flops, compulsory, per_kernel
@@ -197,7 +203,40 @@ def main():
 
     def step(t, events=None):
         vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, True, lse=t["lse"], dq=t["dq"], dk=t["dk"], dv=t["dv"],
-                     workspace=t["ws"], stream=stream, events=events)
+                     workspace=t["ws"], stream=torch.cuda.current_stream(), events=events)
+
+    def capture(setlist):
+        """One HIP graph holding one step per entry of setlist, captured on a side stream."""
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step(setlist[0])
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            for t in setlist:
+                step(t)
+        torch.cuda.synchronize()
+        return g
+
+    def graph_timed(nsteps, rot):
+        """ms per step of nsteps steps (rotating over `rot` sets) replayed from one graph."""
+        g = capture([sets[i % rot] for i in range(nsteps)])
+        g.replay()                                        # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        ref = {n: sets[0][n].clone() for n in ("dq", "dk", "dv")}
+        step(sets[0])                                     # eager call on the same inputs
+        torch.cuda.synchronize()
+        same = all(torch.equal(ref[n], sets[0][n]) for n in ref)
+        start, stop = hip.create(2)
+        hip.record(start, sptr)
+        g.replay()
+        hip.record(stop, sptr)
+        torch.cuda.synchronize()
+        total = hip.ms(start, stop)
+        hip.destroy([start, stop])
+        return total / nsteps, same
 
     def timed(nsteps, rot):
         phase = hip.create(4 * nsteps)
@@ -220,8 +259,13 @@ def main():
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    ms_step, kern_us = timed(args.steps, nsets)
-    warm_ms, warm_us = timed(max(10, args.steps // 2), 1)
+    eager_ms, kern_us = timed(args.steps, nsets)          # per-pass times from eager steps
+    warm_eager_ms, warm_us = timed(max(10, args.steps // 2), 1)
+    ms_step, same = graph_timed(args.steps, nsets)
+    warm_ms, same_w = graph_timed(max(10, args.steps // 2), 1)
+    if not (same and same_w):                             # graph replay must match eager calls
+        print("bench.py: graph replay differs from eager calls; reporting eager timing", file=sys.stderr)
+        ms_step, warm_ms = eager_ms, warm_eager_ms
 
     tflops = flops / (ms_step * 1e-3) / 1e12
     dom = max(kern_us, key=kern_us.get)                   # dominant kernel of the step
@@ -248,11 +292,13 @@ def main():
         "hbm_gbps": round(compulsory / (ms_step * 1e-3) / 1e9, 1),
         "frac_bf16_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "timing": "hip graph replay" if (same and same_w) else "eager",
+        "eager_ms_per_step": round(eager_ms, 5),
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(flops / (warm_ms * 1e-3) / 1e12, 2),
                  "kernel_us": {k: round(v, 2) for k, v in warm_us.items()}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"flash_{dom}_kernel (bf16, d128)",
+                     "kernel": f"{dom}_mfma_kernel (bf16, d128)",
                      "algorithmic_bytes": per_kernel[dom]["bytes"],
                      "algorithmic_flops": per_kernel[dom]["flops"],
                      "mfma_tflops": round(per_kernel[dom]["flops"] / dom_s / 1e12, 1),

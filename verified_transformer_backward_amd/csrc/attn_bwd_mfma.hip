@@ -11,6 +11,11 @@
 //         so the sweep accumulates A = (P o dP) K, B = P K and D = rowsum(P o dP)
 //         together and forms dQ = scale (A - D B) at the end: four contractions per
 //         key block instead of two sweeps of five. Writes dQ and D.
+//         The D used for dQ sums the same bf16-rounded (P o dP) values that enter A, so
+//         the rounding of each term cancels against B: dQ_i carries errors
+//         delta_ij (k_j - B_i) rather than delta_ij k_j, and a row whose dS vanishes
+//         (a single visible key) gets dQ = 0 exactly. The D written for the dk/dv pass
+//         is the fp32 sum, exact enough that dS = P o (dP - D) vanishes there too.
 //   dkdv  key-parallel over query blocks (of every q-head of the kv-head's group):
 //         S, dP, then dV += P^T dO and dK += dS^T Q with dS = P o (dP - D), D from dq.
 //
@@ -204,9 +209,9 @@ void dq_mfma_kernel(AttnParams p) {
       acA[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       acB[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  float dsum[kNT];
+  float dsum[kNT], dsum_r[kNT];   // D from fp32 P o dP, and from its bf16 rounding
 #pragma unroll
-  for (int qt = 0; qt < kNT; ++qt) dsum[qt] = 0.f;
+  for (int qt = 0; qt < kNT; ++qt) dsum[qt] = dsum_r[qt] = 0.f;
 
   const int last_row = min(Tq, (qb + 1) * BM) - 1;
   const int kend = p.causal ? min(Tk, last_row + off + 1) : Tk;
@@ -282,9 +287,11 @@ void dq_mfma_kernel(AttnParams p) {
             pr = ((jj < Tk) & (!p.causal | (jj <= i + off))) ? pr : 0.f;
           }
           const float x = pr * dT[kt][qt][r];
+          const __bf16 xr = (__bf16)x;
           dsum[qt] += x;
+          dsum_r[qt] += (float)xr;
           pb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)pr;
-          xb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)x;
+          xb[kt >> 1][qt][4 * (kt & 1) + r] = xr;
         }
     fence();
     // A^T += K^T (P o dP)^T,  B^T += K^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
@@ -336,10 +343,12 @@ void dq_mfma_kernel(AttnParams p) {
   float Dq[kNT];
 #pragma unroll
   for (int qt = 0; qt < kNT; ++qt) {
-    float d = dsum[qt];
+    float d = dsum[qt], dr = dsum_r[qt];
     d += __shfl_xor(d, 16, 64);
     d += __shfl_xor(d, 32, 64);
-    Dq[qt] = d;
+    dr += __shfl_xor(dr, 16, 64);
+    dr += __shfl_xor(dr, 32, 64);
+    Dq[qt] = dr;
     const int i = qw0 + 16 * qt + lc;
     if (lg == 0 && i < Tq) p.dlt[rowbase + i] = d;
   }
