@@ -58,20 +58,32 @@ def test_rmsnorm_shapes(rows, n):
     assert_close("rmsnorm", host(out), L.rmsnorm_backward_rows(x, g, dy, 1e-6), TOL["f32"])
 
 
-def test_fused_rope_rmsnorm_residual():
+FUSED_CASES = [
+    # T, H, d, layout, pos0, in place  (the first two take the float4 path, the rest the scalar one)
+    (256, 20, 128, 0, 0, False),
+    (33, 3, 64, 1, 100, False),
+    (8, 32, 128, 1, 8000, True),
+    (17, 5, 6, 0, 7, False),
+    (40, 2, 12, 1, 3, True),
+]
+
+
+@pytest.mark.parametrize("T,H,d,layout,pos0,inplace", FUSED_CASES)
+def test_fused_rope_rmsnorm_residual(T, H, d, layout, pos0, inplace):
     need_gpu()
-    say("fused rope+rmsnorm+residual T 256 C 2560")
-    rng = np.random.default_rng(4)
-    T, H, d = 256, 20, 128
+    say(f"fused rope+rmsnorm+residual T {T} H {H} d {d} layout {layout} pos0 {pos0} in-place {inplace}")
+    rng = np.random.default_rng(4 + T + d)
     C = H * d
     dq = rng.standard_normal((T, C)).astype(np.float32)
     x = rng.standard_normal((T, C)).astype(np.float32)
     g = rng.standard_normal((T, C)).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, C).astype(np.float32)
     sc = 0.25
-    dn = L.rope_backward_rows((sc * dq.astype(np.float64)).reshape(T, H, d), np.arange(T))
+    dn = L.rope_backward_rows((sc * dq.astype(np.float64)).reshape(T, H, d), pos0 + np.arange(T), layout=layout)
     ref = g + L.rmsnorm_backward_rows(x, gamma, dn.reshape(T, C), 1e-6)
-    out = vtb.rope_rmsnorm_res_bwd(dev(dq), dev(x), dev(gamma), dev(g), H, d, dq_scale=sc)
+    gd = dev(g)
+    out = vtb.rope_rmsnorm_res_bwd(dev(dq), dev(x), dev(gamma), gd, H, d, dq_scale=sc, pos0=pos0, layout=layout,
+                                   dh_in=gd if inplace else None)
     torch.cuda.synchronize()
     assert_close("fused", host(out), ref, TOL["f32"])
 

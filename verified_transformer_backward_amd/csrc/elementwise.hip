@@ -11,6 +11,9 @@
 // Residual: the hidden gradient passes through unchanged and the branch gradient is
 // added (Hesper commit log, residual backward).
 #include "device_common.h"
+
+#include <cmath>
+#include <cstdint>
 #include "launch.h"
 
 namespace vtb {
@@ -180,6 +183,111 @@ __global__ __launch_bounds__(256) void rope_rmsnorm_res_kernel(const float* __re
   }
 }
 
+// Vector form of the fused tail (row width a multiple of 4, heads split into whole
+// float4s, 16-byte aligned rows). One workgroup per token row:
+//  * every global load of the row is issued first, unconditionally (indices clamped);
+//  * meanwhile the first head_dim/2 threads build the row's (cos, sin) table in LDS, one
+//    angle per frequency instead of one per pair: theta_i = p * 2^(-(2i/d) log2 base),
+//    formed and reduced modulo 2 pi in fp64, sin/cos in fp32;
+//  * rotation, the two RMSNorm row sums, one block reduction, and float4 stores.
+// LAYOUT 0 pairs (2i, 2i+1): a float4 holds two pairs. LAYOUT 1 pairs (i, i + d/2): a unit
+// is the float4 at i and the float4 at i + d/2 of the same head, four pairs.
+template <int LAYOUT, int NV>
+__global__ __launch_bounds__(256) void rope_rmsnorm_res_vec_kernel(const float4* __restrict__ dq, float dq_scale,
+                                                                   const float4* __restrict__ x,
+                                                                   const float4* __restrict__ gamma, const float4* dh_out,
+                                                                   float4* dh_in, int n_heads, int hd, int pos0,
+                                                                   double log2_base, float eps) {
+  extern __shared__ float2 cs[];   // [hd / 2] (cos, sin) of this row's angles
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int C = n_heads * hd, C4 = C / 4, hd4 = hd / 4;
+  const int units = LAYOUT == 0 ? C4 : C4 / 2;
+  const int64_t ro = (int64_t)t * C4;
+  float4 qa[NV], qb[NV], xa[NV], xb[NV], ga[NV], gb[NV], ha[NV], hb[NV];
+  int ia[NV], ib[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int u = min(tid + 256 * e, units - 1);
+    if (LAYOUT == 0) {
+      ia[e] = u;
+      ib[e] = u;
+    } else {
+      const int h = u / (hd4 / 2), j = u % (hd4 / 2);
+      ia[e] = h * hd4 + j;
+      ib[e] = ia[e] + hd4 / 2;
+    }
+    qa[e] = dq[ro + ia[e]];
+    xa[e] = x[ro + ia[e]];
+    ha[e] = dh_out[ro + ia[e]];
+    ga[e] = gamma[ia[e]];
+    if (LAYOUT == 1) {
+      qb[e] = dq[ro + ib[e]];
+      xb[e] = x[ro + ib[e]];
+      hb[e] = dh_out[ro + ib[e]];
+      gb[e] = gamma[ib[e]];
+    }
+  }
+  const int half = hd / 2;
+  const double pp = (double)pos0 + t;
+  for (int i = tid; i < half; i += 256) {
+    float sn, cn;
+    rope_sincos(pp * exp2(-(2.0 * i / hd) * log2_base), &sn, &cn);
+    cs[i] = make_float2(cn, sn);
+  }
+  __syncthreads();
+  float ss = 0.f, cc = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const bool on = tid + 256 * e < units;
+    if (LAYOUT == 0) {
+      const int i0 = ((4 * ia[e]) % hd) / 2;
+      const float2 c0 = cs[i0], c1 = cs[i0 + 1];
+      const float y0 = qa[e].x * dq_scale, y1 = qa[e].y * dq_scale, y2 = qa[e].z * dq_scale, y3 = qa[e].w * dq_scale;
+      qa[e] = make_float4(y0 * c0.x + y1 * c0.y, -y0 * c0.y + y1 * c0.x, y2 * c1.x + y3 * c1.y, -y2 * c1.y + y3 * c1.x);
+      if (on) {
+        ss += xa[e].x * xa[e].x + xa[e].y * xa[e].y + xa[e].z * xa[e].z + xa[e].w * xa[e].w;
+        cc += qa[e].x * ga[e].x * xa[e].x + qa[e].y * ga[e].y * xa[e].y + qa[e].z * ga[e].z * xa[e].z +
+              qa[e].w * ga[e].w * xa[e].w;
+      }
+    } else {
+      const int i0 = 4 * (ia[e] % hd4);
+      const float ya[4] = {qa[e].x * dq_scale, qa[e].y * dq_scale, qa[e].z * dq_scale, qa[e].w * dq_scale};
+      const float yb[4] = {qb[e].x * dq_scale, qb[e].y * dq_scale, qb[e].z * dq_scale, qb[e].w * dq_scale};
+      float ra[4], rb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 c = cs[i0 + k];
+        ra[k] = ya[k] * c.x + yb[k] * c.y;
+        rb[k] = -ya[k] * c.y + yb[k] * c.x;
+      }
+      qa[e] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+      qb[e] = make_float4(rb[0], rb[1], rb[2], rb[3]);
+      if (on) {
+        ss += xa[e].x * xa[e].x + xa[e].y * xa[e].y + xa[e].z * xa[e].z + xa[e].w * xa[e].w +
+              xb[e].x * xb[e].x + xb[e].y * xb[e].y + xb[e].z * xb[e].z + xb[e].w * xb[e].w;
+        cc += qa[e].x * ga[e].x * xa[e].x + qa[e].y * ga[e].y * xa[e].y + qa[e].z * ga[e].z * xa[e].z +
+              qa[e].w * ga[e].w * xa[e].w + qb[e].x * gb[e].x * xb[e].x + qb[e].y * gb[e].y * xb[e].y +
+              qb[e].z * gb[e].z * xb[e].z + qb[e].w * gb[e].w * xb[e].w;
+      }
+    }
+  }
+  const float2 tot = block_sum2(ss, cc);
+  const float r2 = tot.x / C + eps;
+  const float rinv = rsqrtf(r2);
+  const float coef = tot.y / (C * r2);
+  auto out = [&](const float4& y, const float4& g, const float4& xx, const float4& h) {
+    return make_float4(h.x + (y.x * g.x - xx.x * coef) * rinv, h.y + (y.y * g.y - xx.y * coef) * rinv,
+                       h.z + (y.z * g.z - xx.z * coef) * rinv, h.w + (y.w * g.w - xx.w * coef) * rinv);
+  };
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    if (tid + 256 * e < units) {
+      dh_in[ro + ia[e]] = out(qa[e], ga[e], xa[e], ha[e]);
+      if (LAYOUT == 1) dh_in[ro + ib[e]] = out(qb[e], gb[e], xb[e], hb[e]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* x, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) x[i] = 0.f;
 }
@@ -225,6 +333,31 @@ hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const fl
                                        const float* dh_out, float* dh_in, int T, int n_heads, int head_dim, int pos0,
                                        double base, int layout, float eps, hipStream_t s) {
   const int npairs = n_heads * head_dim / 2;
+  const int C = n_heads * head_dim;
+  const bool vec = C % 4 == 0 && (layout == 0 ? head_dim % 4 == 0 : head_dim % 8 == 0) &&
+                   ((uintptr_t)dq | (uintptr_t)x | (uintptr_t)gamma | (uintptr_t)dh_out | (uintptr_t)dh_in) % 16 == 0;
+  if (vec) {
+    const int units = layout == 0 ? C / 4 : C / 8;
+    const int nv = (units + 255) / 256;   // 1 .. 4 (rows hold at most 4096 values)
+    const size_t lds = (size_t)(head_dim / 2) * sizeof(float2);
+    const double l2b = std::log2(base);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(T), dim3(256), lds, s, reinterpret_cast<const float4*>(dq), dq_scale,
+                         reinterpret_cast<const float4*>(x), reinterpret_cast<const float4*>(gamma),
+                         reinterpret_cast<const float4*>(dh_out), reinterpret_cast<float4*>(dh_in), n_heads, head_dim, pos0,
+                         l2b, eps);
+    };
+    if (layout == 0) {
+      if (nv <= 1) go(rope_rmsnorm_res_vec_kernel<0, 1>);
+      else if (nv <= 2) go(rope_rmsnorm_res_vec_kernel<0, 2>);
+      else go(rope_rmsnorm_res_vec_kernel<0, 4>);
+    } else {
+      if (nv <= 1) go(rope_rmsnorm_res_vec_kernel<1, 1>);
+      else if (nv <= 2) go(rope_rmsnorm_res_vec_kernel<1, 2>);
+      else go(rope_rmsnorm_res_vec_kernel<1, 4>);
+    }
+    return hipGetLastError();
+  }
   if (npairs <= 256 * 2)
     hipLaunchKernelGGL(rope_rmsnorm_res_kernel<2>, dim3(T), dim3(256), 0, s, dq, dq_scale, x, gamma, dh_out, dh_in,
                        n_heads, head_dim, pos0, base, layout, eps);
