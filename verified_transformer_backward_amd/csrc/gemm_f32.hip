@@ -30,60 +30,68 @@ struct GemmDesc {
   int vec;         // float4 loads are valid along the contiguous dimensions
 };
 
-// Stage rows [r0, r0+64) x k [k0, k0+KT) of an operand X(r, k) = X[r*sr + k*sk] into
-// tile[r][k]. kc: X is k-contiguous (sk == 1); else r-contiguous (sr == 1).
-__device__ __forceinline__ void stage(float* tile, const float* X, int64_t sr, int64_t sk, int kc, int vec, int r0,
-                                      int k0, int R, int K) {
-  const int tid = threadIdx.x;
-  if (kc) {
+// One operand tile, rows [r0, r0+64) x k [k0, k0+KT) of X(r, k) = X[r*sr + k*sk], held
+// in registers between its global loads and its LDS store (two 16-byte chunks per
+// thread). load() issues every load at once, always in bounds (indices clamped, an
+// element outside the matrix is zeroed by store()), so the loads of the next k step
+// run under the current step's MFMAs. store() writes tile[r][k] (k-contiguous rows),
+// transposing when X is r-contiguous.
+struct OpRegs {
+  float4 v[2];
+  unsigned valid;   // bit 4e + i: element i of chunk e is inside the matrix
+  __device__ __forceinline__ void load(const float* X, int64_t sr, int64_t sk, int kc, int vec, int r0, int k0, int R,
+                                       int K) {
+    const int tid = threadIdx.x;
+    valid = 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;  // 64 rows x 8 float4
-      const int r = idx >> 3, kq = (idx & 7) * 4;
-      const int gr = r0 + r, gk = k0 + kq;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (gr < R) {
-        const float* src = X + (int64_t)gr * sr + gk;
-        if (vec) {
-          if (gk < K) v = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (gk < K) v.x = src[0];
-          if (gk + 1 < K) v.y = src[1];
-          if (gk + 2 < K) v.z = src[2];
-          if (gk + 3 < K) v.w = src[3];
-        }
-      }
-      *reinterpret_cast<float4*>(tile + r * LDT + kq) = v;
-    }
-  } else {
+      const int idx = tid + 256 * e;
+      // kc: 64 rows x 8 chunks of 4 k;  !kc: KT k x 16 chunks of 4 rows
+      const int gr = kc ? r0 + (idx >> 3) : r0 + (idx & 15) * 4;
+      const int gk = kc ? k0 + (idx & 7) * 4 : k0 + (idx >> 4);
+      if (vec) {
+        const int cr = min(gr, R - (kc ? 1 : 4)), ck = min(gk, K - (kc ? 4 : 1));
+        v[e] = *reinterpret_cast<const float4*>(X + (int64_t)cr * sr + (int64_t)ck * sk);
+        if (gr < R && gk < K) valid |= 0xFu << (4 * e);
+      } else {
+        float t[4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;  // KT k-rows x 16 float4 along r
-      const int k = idx >> 4, rq = (idx & 15) * 4;
-      const int gr = r0 + rq, gk = k0 + k;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (gk < K) {
-        const float* src = X + (int64_t)gk * sk + gr;
-        if (vec) {
-          if (gr < R) v = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (gr < R) v.x = src[0];
-          if (gr + 1 < R) v.y = src[1];
-          if (gr + 2 < R) v.z = src[2];
-          if (gr + 3 < R) v.w = src[3];
+        for (int i = 0; i < 4; ++i) {
+          const int rr = kc ? gr : gr + i, kk = kc ? gk + i : gk;
+          t[i] = X[(int64_t)min(rr, R - 1) * sr + (int64_t)min(kk, K - 1) * sk];
+          if (rr < R && kk < K) valid |= 1u << (4 * e + i);
         }
+        v[e] = make_float4(t[0], t[1], t[2], t[3]);
       }
-      tile[(rq + 0) * LDT + k] = v.x;
-      tile[(rq + 1) * LDT + k] = v.y;
-      tile[(rq + 2) * LDT + k] = v.z;
-      tile[(rq + 3) * LDT + k] = v.w;
     }
   }
-}
+  __device__ __forceinline__ void store(float* tile, int kc) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + 256 * e;
+      const unsigned m = valid >> (4 * e);
+      const float4 x = make_float4(m & 1u ? v[e].x : 0.f, m & 2u ? v[e].y : 0.f, m & 4u ? v[e].z : 0.f,
+                                   m & 8u ? v[e].w : 0.f);
+      if (kc) {
+        *reinterpret_cast<float4*>(tile + (idx >> 3) * LDT + (idx & 7) * 4) = x;
+      } else {
+        const int k = idx >> 4, rq = (idx & 15) * 4;
+        tile[(rq + 0) * LDT + k] = x.x;
+        tile[(rq + 1) * LDT + k] = x.y;
+        tile[(rq + 2) * LDT + k] = x.z;
+        tile[(rq + 3) * LDT + k] = x.w;
+      }
+    }
+  }
+};
 
+// Tiles of two GEMMs in one grid: blocks [0, tiles0) compute d0, the rest d1. Per k
+// step: one barrier (step k in LDS, step k-1 retired), the next step's loads issued into
+// registers, this step's MFMAs, then the registers stored into the other LDS buffer.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, int tiles0) {
-  __shared__ __attribute__((aligned(32))) float sA[BMG * LDT];
-  __shared__ __attribute__((aligned(32))) float sB[BNG * LDT];
+  __shared__ __attribute__((aligned(32))) float sA[2][BMG * LDT];
+  __shared__ __attribute__((aligned(32))) float sB[2][BNG * LDT];
   const bool first = (int)blockIdx.x < tiles0;
   const GemmDesc& d = first ? d0 : d1;
   const int tile = first ? blockIdx.x : blockIdx.x - tiles0;
@@ -98,20 +106,34 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1,
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < d.K; k0 += KT) {
+  OpRegs ra, rb;
+  ra.load(d.A, d.am, d.ak, d.a_kc, d.vec, m0, 0, d.M, d.K);
+  rb.load(d.B, d.bn, d.bk, d.b_kc, d.vec, n0, 0, d.N, d.K);
+  ra.store(sA[0], d.a_kc);
+  rb.store(sB[0], d.b_kc);
+  const int nk = (d.K + KT - 1) / KT;
+  for (int s = 0; s < nk; ++s) {
     __syncthreads();
-    stage(sA, d.A, d.am, d.ak, d.a_kc, d.vec, m0, k0, d.M, d.K);
-    stage(sB, d.B, d.bn, d.bk, d.b_kc, d.vec, n0, k0, d.N, d.K);
-    __syncthreads();
+    const bool more = s + 1 < nk;
+    if (more) {
+      ra.load(d.A, d.am, d.ak, d.a_kc, d.vec, m0, (s + 1) * KT, d.M, d.K);
+      rb.load(d.B, d.bn, d.bk, d.b_kc, d.vec, n0, (s + 1) * KT, d.N, d.K);
+    }
+    const float* a_t = sA[s & 1];
+    const float* b_t = sB[s & 1];
     f32x8 a[2], b[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = load8<float>(sA + (wm + 16 * i + lc) * LDT + 8 * lg);
+    for (int i = 0; i < 2; ++i) a[i] = load8<float>(a_t + (wm + 16 * i + lc) * LDT + 8 * lg);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = load8<float>(sB + (wn + 16 * j + lc) * LDT + 8 * lg);
+    for (int j = 0; j < 2; ++j) b[j] = load8<float>(b_t + (wn + 16 * j + lc) * LDT + 8 * lg);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], b[j]);
+    if (more) {
+      ra.store(sA[(s + 1) & 1], d.a_kc);
+      rb.store(sB[(s + 1) & 1], d.b_kc);
+    }
   }
 
 #pragma unroll
@@ -131,6 +153,8 @@ int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG -
 
 hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K, int N,
                              hipStream_t s) {
+  // The kernel's clamped loads need every extent, the contraction included, >= 1.
+  if (T < 1 || K < 1 || N < 1) return hipErrorInvalidValue;
   // dX(t, k) = sum_n dY(t, n) W(k, n): A = dY (k-contiguous), B(n_c, k_out) = W[k_out*N + n_c]
   GemmDesc gx{};
   gx.A = dy; gx.am = N; gx.ak = 1; gx.a_kc = 1;
