@@ -110,46 +110,49 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 // Direct-to-LDS staging of 64 rows of one head into a swizzled 64 x 128 tile. Wave w
 // writes rows RPW w .. RPW w + RPW - 1, four rows (1 KB) per load: lane l lands at
 // physical chunk l % 16 of row 4i + l / 16 and so fetches the logical chunk the swizzle
-// keeps there. The lane part of the source offset only depends on the parity of i.
+// keeps there. The lane's byte offsets from the block's first row are fixed for the
+// whole kernel (the row stride is), so a full block costs one 64-bit row address and,
+// per load, a scalar add for M0.
 struct RowStager {
   static constexpr int RPW = kRows / kW;
   static constexpr int NI = RPW / 4;
-  int loff[2];   // lane offsets (elements) for even / odd i
+  uint32_t voff[NI];   // byte offset of the lane's 16 bytes for load i, from row t0
   int w;
   __device__ __forceinline__ void init(int wave, int64_t tstride) {
     w = wave;
-    const int lane = threadIdx.x & 63, sub = lane >> 4, pc = lane & 15;
-    const int hbit = ((RPW * w) >> 4) & 1;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-      loff[par] = sub * (int)tstride + 8 * (pc ^ ((((4 * par + sub) & 7) << 1) | hbit));
-  }
-  // Load i (0 .. NI-1) of rows [t0, t0 + 64) of `head` (row t at head + t * tstride);
-  // rows >= tlimit read row tlimit - 1.
-  __device__ __forceinline__ void stage_one(__bf16* tile, const __bf16* head, int64_t tstride, int t0, int tlimit,
-                                            int i) const {
-    if (t0 + kRows <= tlimit) {
-      const __bf16* rowp = head + (int64_t)(t0 + RPW * w + 4 * i) * tstride;
-      dma16(rowp, 2u * (uint32_t)loff[i & 1], lds_addr(tile + (RPW * w + 4 * i) * kHD));
-    } else {
-      const int lane = threadIdx.x & 63;
+    for (int i = 0; i < NI; ++i) {
       const int row = RPW * w + 4 * i + (lane >> 4);
-      const int t = min(t0 + row, tlimit - 1) - t0;   // 0 .. 63
-      const uint32_t voff = 2u * (uint32_t)(t * (int)tstride + 8 * ((lane & 15) ^ LT::chunk_xor(row)));
-      dma16(head + (int64_t)t0 * tstride, voff, lds_addr(tile + (RPW * w + 4 * i) * kHD));
+      voff[i] = 2u * (uint32_t)(row * (int)tstride + 8 * ((lane & 15) ^ LT::chunk_xor(row)));
     }
   }
-  __device__ __forceinline__ void stage(__bf16* tile, const __bf16* head, int64_t tstride, int t0, int tlimit) const {
+  // Rows [t0, t0 + 64) of `head` (row t at head + t * tstride) into the tile at LDS byte
+  // address `tile`; rows >= tlimit read row tlimit - 1.
+  __device__ __forceinline__ void stage(uint32_t tile, const __bf16* head, int64_t tstride, int t0, int tlimit) const {
+    const __bf16* row0 = head + (int64_t)t0 * tstride;
+    const uint32_t dst = tile + 2u * (uint32_t)(RPW * w * kHD);
+    if (t0 + kRows <= tlimit) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) stage_one(tile, head, tstride, t0, tlimit, i);
+      for (int i = 0; i < NI; ++i) dma16(row0, voff[i], dst + 2u * (uint32_t)(4 * i * kHD));
+    } else {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = RPW * w + 4 * i + (lane >> 4);
+        const int t = min(t0 + row, tlimit - 1) - t0;   // 0 .. 63
+        const uint32_t vo = 2u * (uint32_t)(t * (int)tstride + 8 * ((lane & 15) ^ LT::chunk_xor(row)));
+        dma16(row0, vo, dst + 2u * (uint32_t)(4 * i * kHD));
+      }
+    }
   }
 };
 
-// 64 consecutive fp32 values src[i0 .. i0 + 63] (indices clamped to n - 1) into LDS, one
-// direct-to-LDS dword per lane; called by a single wave.
-__device__ __forceinline__ void stage_vals64(float* dst, const float* src, int i0, int n) {
+// 64 consecutive fp32 values src[i0 .. i0 + 63] (indices clamped to n - 1) into LDS at
+// byte address dst, one direct-to-LDS dword per lane; called by a single wave.
+__device__ __forceinline__ void stage_vals64(uint32_t dst, const float* src, int i0, int n) {
   const int lane = threadIdx.x & 63;
-  dma4(src + i0, 4u * (uint32_t)(min(i0 + lane, n - 1) - i0), lds_addr(dst));
+  dma4(src + i0, 4u * (uint32_t)(min(i0 + lane, n - 1) - i0), dst);
 }
 
 // Four consecutive output elements (fp32 or bf16 RNE).
@@ -226,11 +229,13 @@ void dq_mfma_kernel(AttnParams p) {
   // The register loads above complete before any direct-to-LDS load is issued, so the
   // compiler needs no waits for them inside the loop (it does not see the LDS loads).
   wait_loads();
+  const uint32_t sm_lds = lds_addr(&sm[0][0][0]);
+  constexpr uint32_t kTileBytes = 2u * BN * kHD;
 #pragma unroll
   for (int s = 0; s < kBufs - 1; ++s)
     if (s < nblk) {
-      kst.stage(sm[s][0], Kh, p.sk[1], s * BN, Tk);
-      vst.stage(sm[s][1], Vh, p.sv[1], s * BN, Tk);
+      kst.stage(sm_lds + (2 * s) * kTileBytes, Kh, p.sk[1], s * BN, Tk);
+      vst.stage(sm_lds + (2 * s + 1) * kTileBytes, Vh, p.sv[1], s * BN, Tk);
     }
   int cur = 0;   // buffer of block j
 
@@ -322,8 +327,8 @@ void dq_mfma_kernel(AttnParams p) {
     const int tn = jb + (kBufs - 1) * BN;
     auto dma = [&](int part) {
       if (!more || part != 0) return;
-      kst.stage(sm[nxt][0], Kh, p.sk[1], tn, Tk);
-      vst.stage(sm[nxt][1], Vh, p.sv[1], tn, Tk);
+      kst.stage(sm_lds + (2 * nxt) * kTileBytes, Kh, p.sk[1], tn, Tk);
+      vst.stage(sm_lds + (2 * nxt + 1) * kTileBytes, Vh, p.sv[1], tn, Tk);
     };
     const int bj = cur;
     cur = cur + 1 == kBufs ? 0 : cur + 1;
@@ -419,14 +424,17 @@ void dkdv_mfma_kernel(AttnParams p) {
   RowStager qst, ost;
   qst.init(w, p.sq[1]);
   ost.init(w, p.sdo[1]);
+  const uint32_t sm_lds = lds_addr(&sm[0][0][0]);
+  const uint32_t sv_lds = lds_addr(&sv[0][0][0]);
+  constexpr uint32_t kTileBytes = 2u * BM * kHD, kValBytes = 4u * BM;
   auto stage = [&](int buf, int hh, int q0) {
     const __bf16* Qh = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)hh * p.sq[2];
     const __bf16* Oh = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.sdo[0] + (int64_t)hh * p.sdo[2];
-    qst.stage(sm[buf][0], Qh, p.sq[1], q0, Tq);
-    ost.stage(sm[buf][1], Oh, p.sdo[1], q0, Tq);
+    qst.stage(sm_lds + (2 * buf) * kTileBytes, Qh, p.sq[1], q0, Tq);
+    ost.stage(sm_lds + (2 * buf + 1) * kTileBytes, Oh, p.sdo[1], q0, Tq);
     const int64_t rb = ((int64_t)b * p.Hq + hh) * Tq;
-    if (w == 0) stage_vals64(sv[buf][0], p.lse + rb, q0, Tq);
-    if (w == 1) stage_vals64(sv[buf][1], p.dlt + rb, q0, Tq);
+    if (w == 0) stage_vals64(sv_lds + (2 * buf) * kValBytes, p.lse + rb, q0, Tq);
+    if (w == 1) stage_vals64(sv_lds + (2 * buf + 1) * kValBytes, p.dlt + rb, q0, Tq);
   };
 
   auto block = [&](int buf, int q0, auto full_tag, auto&& dma) {
@@ -548,10 +556,10 @@ void dkdv_mfma_kernel(AttnParams p) {
     auto dma = [&](int part) {
       if (!more || part != 0) return;
       const int64_t rb = ((int64_t)b * p.Hq + hs) * Tq;
-      if (w == 0) stage_vals64(sv[nxt][0], p.lse + rb, qn, Tq);
-      if (w == 1) stage_vals64(sv[nxt][1], p.dlt + rb, qn, Tq);
-      qst.stage(sm[nxt][0], Qn, p.sq[1], qn, Tq);
-      ost.stage(sm[nxt][1], On, p.sdo[1], qn, Tq);
+      if (w == 0) stage_vals64(sv_lds + (2 * nxt) * kValBytes, p.lse + rb, qn, Tq);
+      if (w == 1) stage_vals64(sv_lds + (2 * nxt + 1) * kValBytes, p.dlt + rb, qn, Tq);
+      qst.stage(sm_lds + (2 * nxt) * kTileBytes, Qn, p.sq[1], qn, Tq);
+      ost.stage(sm_lds + (2 * nxt + 1) * kTileBytes, On, p.sdo[1], qn, Tq);
     };
     const int buf = cur;
     cur = cur + 1 == kBufs ? 0 : cur + 1;
@@ -596,7 +604,11 @@ void dkdv_mfma_kernel(AttnParams p) {
 
 }  // namespace
 
-bool mfma_path_applicable(const AttnParams& p) { return p.in_bf16 && p.D == kHD; }
+bool mfma_path_applicable(const AttnParams& p) {
+  // The staging loads address a 64-row block with 32-bit byte offsets from its first row.
+  auto small = [](int64_t st) { return st >= 1 && st <= (int64_t)1 << 24; };
+  return p.in_bf16 && p.D == kHD && small(p.sq[1]) && small(p.sk[1]) && small(p.sv[1]) && small(p.sdo[1]);
+}
 
 hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s) {
   constexpr int BM = kW * 16 * kNT;
