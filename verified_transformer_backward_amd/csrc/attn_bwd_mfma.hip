@@ -54,10 +54,10 @@ constexpr int kNT = VTB_MFMA_TILES;
 constexpr int kW = VTB_MFMA_WAVES;
 constexpr int kT = 64 * kW;
 constexpr int kWavesPerEU = kNT == 1 ? 2 : 1;   // register budget: 256 or 512 per lane
-#ifndef VTB_MFMA_BUFS           // staged blocks in flight: loads run NBUF - 1 blocks ahead
-#define VTB_MFMA_BUFS 2
-#endif
-constexpr int kBufs = VTB_MFMA_BUFS;
+// Two staged blocks: the loads of block j + 1 run under block j's MFMAs. The block loops
+// are unrolled by two so that every LDS address is a per-lane base plus a constant.
+template <int B>
+using BufC = std::integral_constant<int, B>;
 static_assert(kW == 4 || kW == 8, "64-row tiles are staged four rows per load by every wave");
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -66,25 +66,6 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // included, has landed. A real waitcnt instruction, so the compiler also knows that its
 // own earlier loads are complete and adds no waits for them inside the block loops.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// s_waitcnt vmcnt(n): at most n vector-memory loads of the wave still in flight. Loads
-// complete in issue order, so this waits for everything but the n youngest.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_vm_upto(int n) {   // n is wave-uniform
-  switch (n) {
-#define VTB_WAIT_CASE(k) case k: wait_vm<k>(); break;
-    VTB_WAIT_CASE(1) VTB_WAIT_CASE(2) VTB_WAIT_CASE(3) VTB_WAIT_CASE(4) VTB_WAIT_CASE(5) VTB_WAIT_CASE(6)
-    VTB_WAIT_CASE(7) VTB_WAIT_CASE(8) VTB_WAIT_CASE(9) VTB_WAIT_CASE(10) VTB_WAIT_CASE(11) VTB_WAIT_CASE(12)
-    VTB_WAIT_CASE(13) VTB_WAIT_CASE(14) VTB_WAIT_CASE(15) VTB_WAIT_CASE(16) VTB_WAIT_CASE(17) VTB_WAIT_CASE(18)
-    VTB_WAIT_CASE(19) VTB_WAIT_CASE(20) VTB_WAIT_CASE(21) VTB_WAIT_CASE(22) VTB_WAIT_CASE(23) VTB_WAIT_CASE(24)
-#undef VTB_WAIT_CASE
-    default: wait_loads(); break;
-  }
-}
 
 // Scheduling fence: keeps the issue order of the operand-read groups written around it,
 // so LDS reads run ahead of the MFMAs that consume them.
@@ -173,7 +154,7 @@ __device__ __forceinline__ void store4(void* base, int bf16, int64_t off, float 
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void dq_mfma_kernel(AttnParams p) {
   constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
-  __shared__ __attribute__((aligned(1024))) __bf16 sm[kBufs][2][BN * kHD];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BN * kHD];   // [buffer][K, V]
 
   const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
   const int nqb = (p.Tq + BM - 1) / BM;
@@ -225,22 +206,19 @@ void dq_mfma_kernel(AttnParams p) {
   RowStager kst, vst;
   kst.init(w, p.sk[1]);
   vst.init(w, p.sv[1]);
-  constexpr int DMA_PER_BLOCK = 2 * RowStager::NI;   // direct-to-LDS loads per wave per block
   // The register loads above complete before any direct-to-LDS load is issued, so the
   // compiler needs no waits for them inside the loop (it does not see the LDS loads).
   wait_loads();
   const uint32_t sm_lds = lds_addr(&sm[0][0][0]);
   constexpr uint32_t kTileBytes = 2u * BN * kHD;
-#pragma unroll
-  for (int s = 0; s < kBufs - 1; ++s)
-    if (s < nblk) {
-      kst.stage(sm_lds + (2 * s) * kTileBytes, Kh, p.sk[1], s * BN, Tk);
-      vst.stage(sm_lds + (2 * s + 1) * kTileBytes, Vh, p.sv[1], s * BN, Tk);
-    }
-  int cur = 0;   // buffer of block j
+  if (nblk > 0) {
+    kst.stage(sm_lds, Kh, p.sk[1], 0, Tk);
+    vst.stage(sm_lds + kTileBytes, Vh, p.sv[1], 0, Tk);
+  }
 
-  auto block = [&](const __bf16* sK, const __bf16* sV, int jb, auto full_tag, auto&& dma) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  auto block = [&](auto buf_c, int jb, bool full, auto&& dma) {
+    const __bf16* sK = sm[decltype(buf_c)::value][0];
+    const __bf16* sV = sm[decltype(buf_c)::value][1];
     // S^T, dP^T: tile kt holds keys jb + 16 kt + 4 lg + r (reg r) for query column lc.
     // The K and V row fragments of tile kt + 1 are read while tile kt's MFMAs run.
     f32x4 sT[4][kNT], dT[4][kNT];
@@ -279,6 +257,27 @@ void dq_mfma_kernel(AttnParams p) {
     fence();
     // P and P o dP as bf16 B operands (k = 32 keys, n = query): element e of operand c
     // is key 32c + 4 lg + e (e < 4) or 32c + 16 + 4 lg + e - 4 (e >= 4).
+    // Only blocks that cross the diagonal or the end of the keys are masked; the branch
+    // covers just the masking, so both kinds of block share registers and MFMA code.
+    float pe[4][kNT][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pe[kt][qt][r] = __builtin_amdgcn_exp2f(sT[kt][qt][r] * sl2 - lse2[qt]);
+    if (!full) {
+      asm volatile("");   // keeps the masking inside the branch (no speculation into full blocks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < kNT; ++qt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = jb + 16 * kt + 4 * lg + r, i = qw0 + 16 * qt + lc;
+            pe[kt][qt][r] = ((jj < Tk) & (!p.causal | (jj <= i + off))) ? pe[kt][qt][r] : 0.f;
+          }
+    }
     bf16x8 pb[2][kNT], xb[2][kNT];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -286,11 +285,7 @@ void dq_mfma_kernel(AttnParams p) {
       for (int qt = 0; qt < kNT; ++qt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float pr = __builtin_amdgcn_exp2f(sT[kt][qt][r] * sl2 - lse2[qt]);
-          if constexpr (!FULL) {
-            const int jj = jb + 16 * kt + 4 * lg + r, i = qw0 + 16 * qt + lc;
-            pr = ((jj < Tk) & (!p.causal | (jj <= i + off))) ? pr : 0.f;
-          }
+          const float pr = pe[kt][qt][r];
           const float x = pr * dT[kt][qt][r];
           const __bf16 xr = (__bf16)x;
           dsum[qt] += x;
@@ -315,34 +310,32 @@ void dq_mfma_kernel(AttnParams p) {
     }
   };
 
-  for (int j = 0; j < nblk; ++j) {
+  // Block j sits in buffer j % 2. After the barrier every wave has finished block j - 1,
+  // so the loads of block j + 1 go to its buffer right away, ahead of block j's MFMAs.
+  auto iteration = [&](int j, auto buf_c) {
+    constexpr int nxt = decltype(buf_c)::value ^ 1;
     const int jb = j * BN;
-    // blocks j + 1 .. j + kBufs - 2 (those issued) may stay in flight
-    wait_vm_upto(DMA_PER_BLOCK * (min(nblk - 1, j + kBufs - 2) - j));
+    wait_loads();
     __syncthreads();   // block j is in LDS; every wave is done with block j - 1
-    // The loads of block j + kBufs - 1 go to the buffer block j - 1 just freed; they are
-    // issued right after the barrier, ahead of this block's MFMAs.
-    const int nxt = cur == 0 ? kBufs - 1 : cur - 1;
-    const bool more = j + kBufs - 1 < nblk;
-    const int tn = jb + (kBufs - 1) * BN;
+    const bool more = j + 1 < nblk;
     auto dma = [&](int part) {
       if (!more || part != 0) return;
-      kst.stage(sm_lds + (2 * nxt) * kTileBytes, Kh, p.sk[1], tn, Tk);
-      vst.stage(sm_lds + (2 * nxt + 1) * kTileBytes, Vh, p.sv[1], tn, Tk);
+      kst.stage(sm_lds + (2 * nxt) * kTileBytes, Kh, p.sk[1], jb + BN, Tk);
+      vst.stage(sm_lds + (2 * nxt + 1) * kTileBytes, Vh, p.sv[1], jb + BN, Tk);
     };
-    const int bj = cur;
-    cur = cur + 1 == kBufs ? 0 : cur + 1;
     if (jb >= wkend) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) dma(part);
-      continue;
+      dma(0);
+      return;
     }
     const bool full = jb + BN <= Tk && (!p.causal || jb + BN - 1 <= qw0 + off);
-    if (full)
-      block(sm[bj][0], sm[bj][1], jb, std::true_type{}, dma);
-    else
-      block(sm[bj][0], sm[bj][1], jb, std::false_type{}, dma);
+    block(buf_c, jb, full, dma);
+  };
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    iteration(j, BufC<0>{});
+    iteration(j + 1, BufC<1>{});
   }
+  if (j < nblk) iteration(j, BufC<0>{});
 
   // D of the lane's queries: the four 16-lane groups hold disjoint key subsets.
   float Dq[kNT];
@@ -383,8 +376,8 @@ void dq_mfma_kernel(AttnParams p) {
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void dkdv_mfma_kernel(AttnParams p) {
   constexpr int BM = kRows, KW = 16 * kNT, BN = kW * KW;
-  __shared__ __attribute__((aligned(1024))) __bf16 sm[kBufs][2][BM * kHD];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float sv[kBufs][2][BM];            // [buffer][lse, D]
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BM * kHD];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float sv[2][2][BM];            // [buffer][lse, D]
 
   const int b = blockIdx.x / p.Hkv, kvh = blockIdx.x % p.Hkv;
   const int kb = blockIdx.y * BN;
@@ -437,8 +430,8 @@ void dkdv_mfma_kernel(AttnParams p) {
     if (w == 1) stage_vals64(sv_lds + (2 * buf + 1) * kValBytes, p.dlt + rb, q0, Tq);
   };
 
-  auto block = [&](int buf, int q0, auto full_tag, auto&& dma) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  auto block = [&](auto buf_c, int q0, bool full, auto&& dma) {
+    constexpr int buf = decltype(buf_c)::value;
     const __bf16* sQ = sm[buf][0];
     const __bf16* sO = sm[buf][1];
     const f32x4* sL4 = reinterpret_cast<const f32x4*>(&sv[buf][0][0]);
@@ -491,6 +484,27 @@ void dkdv_mfma_kernel(AttnParams p) {
     fence();
     // P and dS as bf16 B operands (k = 32 queries, n = key): element e of operand c is
     // query 32c + 4 lg + e (e < 4) or 32c + 16 + 4 lg + e - 4 (e >= 4).
+    // Only blocks that cross the diagonal or a tensor's end are masked; the branch covers
+    // just the masking, so both kinds of block share registers and MFMA code.
+    float pe[4][kNT][4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pe[qt][kt][r] = __builtin_amdgcn_exp2f(S[qt][kt][r] * sl2 - Lv[qt][r] * kLog2e);
+    if (!full) {
+      asm volatile("");   // keeps the masking inside the branch (no speculation into full blocks)
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = q0 + 16 * qt + 4 * lg + r, jj = kw0 + 16 * kt + lc;
+            pe[qt][kt][r] = ((i < Tq) & (jj < Tk) & (!p.causal | (jj <= i + off))) ? pe[qt][kt][r] : 0.f;
+          }
+    }
     bf16x8 pb[2][kNT], sb[2][kNT];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -498,11 +512,7 @@ void dkdv_mfma_kernel(AttnParams p) {
       for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float pr = __builtin_amdgcn_exp2f(S[qt][kt][r] * sl2 - Lv[qt][r] * kLog2e);
-          if constexpr (!FULL) {
-            const int i = q0 + 16 * qt + 4 * lg + r, jj = kw0 + 16 * kt + lc;
-            pr = ((i < Tq) & (jj < Tk) & (!p.causal | (jj <= i + off))) ? pr : 0.f;
-          }
+          const float pr = pe[qt][kt][r];
           pb[qt >> 1][kt][4 * (qt & 1) + r] = (__bf16)pr;
           sb[qt >> 1][kt][4 * (qt & 1) + r] = (__bf16)(pr * (dP[qt][kt][r] - Dv[qt][r]));
         }
@@ -524,32 +534,28 @@ void dkdv_mfma_kernel(AttnParams p) {
     }
   };
 
-  // (head, query block) of the current and the next iteration, advanced without division
+  // Iteration it works on (head h, query block q0); (hs, q0s) is the iteration whose
+  // loads are in flight, one ahead. Both advance without division. The register loads
+  // above complete first: the compiler then needs no waits for them in the loop (it does
+  // not see the direct-to-LDS loads).
   int h = kvh * G, q0 = qb0 * BM;
-  // iterations are prefetched kBufs - 1 ahead; (hs, q0s) walks the staged sequence. The
-  // register loads above complete first: the compiler then needs no waits for them in the
-  // loop (it does not see the direct-to-LDS loads).
   wait_loads();
-  const int dma_per_it = 2 * RowStager::NI + (w < 2 ? 1 : 0);   // direct-to-LDS loads per wave
   int hs = h, q0s = q0;
-#pragma unroll
-  for (int s = 0; s < kBufs - 1; ++s)
-    if (s < n_it) {
-      stage(s, hs, q0s);
-      q0s += BM;
-      if (q0s >= Tq) {
-        q0s = qb0 * BM;
-        ++hs;
-      }
+  if (n_it > 0) {
+    stage(0, hs, q0s);
+    q0s += BM;
+    if (q0s >= Tq) {
+      q0s = qb0 * BM;
+      ++hs;
     }
-  int cur = 0;
-  for (int it = 0; it < n_it; ++it) {
-    wait_vm_upto(dma_per_it * (min(n_it - 1, it + kBufs - 2) - it));
-    __syncthreads();   // block `it` is in LDS; every wave is done with block it - 1
-    // The loads of iteration it + kBufs - 1 go to the buffer iteration it - 1 just freed,
-    // issued right after the barrier, ahead of this iteration's MFMAs.
-    const int nxt = cur == 0 ? kBufs - 1 : cur - 1;
-    const bool more = it + kBufs - 1 < n_it;
+  }
+  // Iteration it sits in buffer it % 2. After the barrier every wave has finished
+  // iteration it - 1, so the loads of it + 1 go to its buffer right away.
+  auto iteration = [&](int it, auto buf_c) {
+    constexpr int nxt = decltype(buf_c)::value ^ 1;
+    wait_loads();
+    __syncthreads();   // iteration it is in LDS; every wave is done with it - 1
+    const bool more = it + 1 < n_it;
     const __bf16* Qn = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)hs * p.sq[2];
     const __bf16* On = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.sdo[0] + (int64_t)hs * p.sdo[2];
     const int qn = q0s;
@@ -561,17 +567,11 @@ void dkdv_mfma_kernel(AttnParams p) {
       qst.stage(sm_lds + (2 * nxt) * kTileBytes, Qn, p.sq[1], qn, Tq);
       ost.stage(sm_lds + (2 * nxt + 1) * kTileBytes, On, p.sdo[1], qn, Tq);
     };
-    const int buf = cur;
-    cur = cur + 1 == kBufs ? 0 : cur + 1;
     if (q0 + BM - 1 >= wq_first && kw0 < Tk) {
       const bool full = q0 + BM <= Tq && kw0 + KW <= Tk && (!p.causal || kw0 + KW - 1 <= q0 + off);
-      if (full)
-        block(buf, q0, std::true_type{}, dma);
-      else
-        block(buf, q0, std::false_type{}, dma);
+      block(buf_c, q0, full, dma);
     } else {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) dma(part);
+      dma(0);
     }
     if (more) {
       q0s += BM;
@@ -582,7 +582,13 @@ void dkdv_mfma_kernel(AttnParams p) {
     }
     q0 += BM;
     if (q0 >= Tq) q0 = qb0 * BM;
+  };
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
+    iteration(it, BufC<0>{});
+    iteration(it + 1, BufC<1>{});
   }
+  if (it < n_it) iteration(it, BufC<0>{});
 
   // dK = scale acc, dV = acc: the lane holds d = 16 dt + 4 lg + r of key kw0 + 16 kt + lc.
 #pragma unroll
