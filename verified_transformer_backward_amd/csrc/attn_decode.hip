@@ -7,17 +7,23 @@
 //
 // The KV cache is split into 64-key chunks (the tiled split-KV statistics idea the
 // Hesper commit log uses for long caches: per-tile max, sum of exponentials, merged
-// afterwards). Three launches:
-//   scores  per (chunk, kv-head, batch): s = scale q.k and dP = dO.v for every row and
-//           key of the chunk, plus per-row chunk statistics m_c = max s,
-//           l_c = sum exp(s - m_c), u_c = sum exp(s - m_c) dP.
-//   grads   per (chunk, kv-head, batch): merges all chunks' statistics into lse (unless
-//           given) and D = rowsum(P o dP) = sum_c exp(m_c - lse) u_c, forms P and dS for
-//           the chunk, writes dV_j = sum_rows P dO and dK_j = scale sum_rows dS q (rows
-//           in fixed head-then-query order) and a per-chunk dQ partial scale dS K.
-//   reduce  dQ = sum over chunks of the partials (fixed order, no atomics).
+// afterwards). Two launches, each touching the cache once:
+//   chunk  per (chunk, kv-head, batch), K and V read once: for every row r and key j
+//          s = scale q.k and dP = dO.v; per-row chunk statistics m_c = max s,
+//          l_c = sum e, u_c = sum e dP with e = exp(s - m_c); and the chunk's two dQ
+//          pieces A_c = sum_j e dP k_j and B_c = sum_j e k_j.
+//   grads  per (chunk, kv-head, batch), no K/V reads: merges the statistics into lse
+//          (unless given) and D = rowsum(P o dP) = sum_c exp(m_c - lse) u_c, forms P and
+//          dS = P o (dP - D) for the chunk from the stored s and dP, and writes
+//          dV_j = sum_rows P dO and dK_j = scale sum_rows dS q (rows in fixed
+//          head-then-query order). Since dS = P o (dP - D),
+//              dQ_r = scale sum_c exp(m_c - lse_r) (A_c - D_r B_c),
+//          summed over chunks in fixed order; the (row, column) outputs of dQ are split
+//          evenly over the chunk workgroups of the kv-head.
 #include "device_common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace vtb {
 namespace {
@@ -25,12 +31,14 @@ namespace {
 constexpr int kCH = 64;        // keys per chunk
 constexpr int kMaxRows = 16;   // query rows per kv-head group
 constexpr int kThreads = 256;
+constexpr int kPreCh = 16;     // chunks whose dQ terms are prefetched into registers
 
 struct DecodeWs {
-  float* s;        // [B, Hq, Tq, Tk] scaled scores (-inf where invisible)
-  float* dp;       // [B, Hq, Tq, Tk]
-  float* stats;    // [B, Hq, Tq, nch, 3] = (m_c, l_c, u_c)
-  float* dq_part;  // [nch, B, Hq, Tq, D]
+  float* s;      // [rows, Tk] scaled scores (-inf where invisible); row = (b Hq + h) Tq + i
+  float* dp;     // [rows, Tk]
+  float* stats;  // [rows, nch, 3] = (m_c, l_c, u_c)
+  float* a;      // [nch, rows, D] sum_j exp(s - m_c) dP k_j over the chunk
+  float* bk;     // [nch, rows, D] sum_j exp(s - m_c) k_j over the chunk
 };
 
 __host__ __device__ inline int64_t align_up(int64_t x) { return (x + 63) / 64 * 64; }
@@ -46,7 +54,9 @@ DecodeWs carve(const AttnParams& p, void* base) {
   f += align_up(rows * p.Tk);
   w.stats = f;
   f += align_up(rows * nch * 3);
-  w.dq_part = f;
+  w.a = f;
+  f += align_up(nch * rows * p.D);
+  w.bk = f;
   return w;
 }
 
@@ -55,40 +65,100 @@ __device__ __forceinline__ const E* rp(const void* base, const int64_t* st, int 
   return reinterpret_cast<const E*>(base) + (int64_t)b * st[0] + (int64_t)t * st[1] + (int64_t)h * st[2];
 }
 
+// Rows r of the group: q-head kvh G + r / Tq, query r % Tq. The R rows of q and dO go to
+// LDS as fp32 (row stride ld), eight elements per load.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void decode_scores_kernel(AttnParams p, DecodeWs ws, int nch) {
-  const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int G = p.Hq / p.Hkv, R = G * p.Tq, Tq = p.Tq, Tk = p.Tk;
-  const int j0 = ch * kCH;
-  __shared__ float sq[kMaxRows][D], sdo[kMaxRows][D];
-  __shared__ float sk[kCH][D + 1], sv[kCH][D + 1];
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < R * D; idx += kThreads) {
-    const int r = idx / D, d = idx % D;
+__device__ __forceinline__ void stage_rows(const AttnParams& p, int b, int kvh, int R, float* sq, float* sdo,
+                                           int ld) {
+  constexpr int C8 = D / 8;
+  const int G = p.Hq / p.Hkv, Tq = p.Tq;
+  for (int idx = threadIdx.x; idx < R * C8; idx += kThreads) {
+    const int r = idx / C8, c8 = idx % C8;
     const int h = kvh * G + r / Tq, i = r % Tq;
-    sq[r][d] = to_f32(rp<E>(p.q, p.sq, b, i, h)[d]);
-    sdo[r][d] = to_f32(rp<E>(p.dout, p.sdo, b, i, h)[d]);
-  }
-  for (int idx = tid; idx < kCH * D; idx += kThreads) {
-    const int jj = idx / D, d = idx % D;
-    const int j = j0 + jj;
-    sk[jj][d] = j < Tk ? to_f32(rp<E>(p.k, p.sk, b, j, kvh)[d]) : 0.f;
-    sv[jj][d] = j < Tk ? to_f32(rp<E>(p.v, p.sv, b, j, kvh)[d]) : 0.f;
-  }
-  __syncthreads();
-  const int jj = tid & 63, rg = tid >> 6;
-  const int j = j0 + jj;
-  for (int r = rg; r < R; r += kThreads / 64) {  // r is uniform across the wave
-    const int h = kvh * G + r / Tq, i = r % Tq;
-    float s = 0.f, dp = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) {
-      s = fmaf(sq[r][d], sk[jj][d], s);
-      dp = fmaf(sdo[r][d], sv[jj][d], dp);
+    const frag_t<E> q8 = load8<E>(rp<E>(p.q, p.sq, b, i, h) + 8 * c8);
+    const frag_t<E> o8 = load8<E>(rp<E>(p.dout, p.sdo, b, i, h) + 8 * c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq[r * ld + 8 * c8 + e] = to_f32(q8[e]);
+      sdo[r * ld + 8 * c8 + e] = to_f32(o8[e]);
     }
-    s *= p.scale;
-    const bool vis = j < Tk && (!p.causal || j <= i + Tk - Tq);
+  }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void decode_chunk_kernel(AttnParams p, DecodeWs ws, int nch) {
+  // Chunk rows padded to D + 4 floats: a lane reading 16 bytes of its own key row and the
+  // 15 other lanes of its group reading theirs cover all 64 banks once.
+  constexpr int LD = D + 4;
+  constexpr int V = 16 / sizeof(E), CV = D / V, NL = kCH * CV / kThreads;   // 16-byte loads
+  static_assert(NL * kThreads == kCH * CV, "chunk loads must tile the workgroup");
+  typedef E vec_t __attribute__((ext_vector_type(V)));
+  const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = p.Hq / p.Hkv, R = G * p.Tq, Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
+  const int j0 = ch * kCH;
+  // LDS sized for the group's R rows (chunk_lds_bytes): q, dO, the chunk (V, then K),
+  // then dP, e and e dP per row and key.
+  extern __shared__ float4 dyn4[];
+  float* sq = reinterpret_cast<float*>(dyn4);
+  float* sdo = sq + R * D;
+  float* skv = sdo + R * D;
+  float* sdp = skv + kCH * LD;
+  float* sw = sdp + R * kCH;
+  float* sx = sw + R * kCH;
+  const int tid = threadIdx.x;
+
+  // K and V of the chunk: every load issued up front, 16 contiguous bytes per lane; rows
+  // past Tk re-read row Tk - 1.
+  vec_t kreg[NL], vreg[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int f = tid + kThreads * i, row = f / CV, cv = f % CV;
+    const int j = min(j0 + row, Tk - 1);
+    kreg[i] = *reinterpret_cast<const vec_t*>(rp<E>(p.k, p.sk, b, j, kvh) + V * cv);
+    vreg[i] = *reinterpret_cast<const vec_t*>(rp<E>(p.v, p.sv, b, j, kvh) + V * cv);
+  }
+  stage_rows<E, D>(p, b, kvh, R, sq, sdo, D);
+  auto to_lds = [&](const vec_t(&reg)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int f = tid + kThreads * i, row = f / CV, cv = f % CV;
+#pragma unroll
+      for (int e4 = 0; e4 < V; e4 += 4)
+        *reinterpret_cast<float4*>(skv + row * LD + V * cv + e4) =
+            make_float4(to_f32(reg[i][e4]), to_f32(reg[i][e4 + 1]), to_f32(reg[i][e4 + 2]), to_f32(reg[i][e4 + 3]));
+    }
+  };
+  // dot product of LDS row x (R-row array, stride D) with the lane's key row, four
+  // independent partial sums
+  auto dot = [&](const float* x, int jj) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int d = 0; d < D; d += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(skv + jj * LD + d);
+      const float4 xv = *reinterpret_cast<const float4*>(x + d);
+      acc.x = fmaf(xv.x, kv.x, acc.x);
+      acc.y = fmaf(xv.y, kv.y, acc.y);
+      acc.z = fmaf(xv.z, kv.z, acc.z);
+      acc.w = fmaf(xv.w, kv.w, acc.w);
+    }
+    return (acc.x + acc.y) + (acc.z + acc.w);
+  };
+  to_lds(vreg);
+  __syncthreads();
+
+  // lane = key jj, wave = rows rg, rg + 4, ...
+  const int jj = tid & 63, rg = tid >> 6, j = j0 + jj;
+  for (int r = rg; r < R; r += 4) sdp[r * kCH + jj] = dot(sdo + r * D, jj);
+  __syncthreads();   // every read of V is done
+  to_lds(kreg);
+  __syncthreads();
+
+  for (int r = rg; r < R; r += 4) {
+    const int h = kvh * G + r / Tq, i = r % Tq;
     const int64_t row = ((int64_t)b * p.Hq + h) * Tq + i;
+    const float s = dot(sq + r * D, jj) * p.scale;
+    const float dp = sdp[r * kCH + jj];
+    const bool vis = j < Tk && (!p.causal || j <= i + off);
     if (j < Tk) {
       ws.s[row * Tk + j] = vis ? s : -INFINITY;
       ws.dp[row * Tk + j] = dp;
@@ -97,6 +167,8 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(AttnParams p, D
     const float e = (vis && m != -INFINITY) ? expf(s - m) : 0.f;
     const float l = wave_sum(e);
     const float u = wave_sum(e * dp);
+    sw[r * kCH + jj] = e;
+    sx[r * kCH + jj] = e * dp;
     if (jj == 0) {
       float* st = ws.stats + (row * nch + ch) * 3;
       st[0] = m;
@@ -104,17 +176,61 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(AttnParams p, D
       st[2] = u;
     }
   }
+  __syncthreads();
+
+  // A_c, B_c: thread = four columns, rows r = rg2, rg2 + RG, ...
+  constexpr int C4 = D / 4, RG = kThreads / C4;
+  const int c4 = tid % C4, rg2 = tid / C4;
+  const int64_t rows = (int64_t)p.B * p.Hq * Tq;
+  for (int r = rg2; r < R; r += RG) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a;
+#pragma unroll 8
+    for (int k = 0; k < kCH; ++k) {
+      const float4 kv = *reinterpret_cast<const float4*>(skv + k * LD + 4 * c4);
+      const float x = sx[r * kCH + k], w = sw[r * kCH + k];
+      a.x = fmaf(x, kv.x, a.x); a.y = fmaf(x, kv.y, a.y); a.z = fmaf(x, kv.z, a.z); a.w = fmaf(x, kv.w, a.w);
+      bb.x = fmaf(w, kv.x, bb.x); bb.y = fmaf(w, kv.y, bb.y); bb.z = fmaf(w, kv.z, bb.z); bb.w = fmaf(w, kv.w, bb.w);
+    }
+    const int h = kvh * G + r / Tq, i = r % Tq;
+    const int64_t o = ((int64_t)ch * rows + ((int64_t)b * p.Hq + h) * Tq + i) * D + 4 * c4;
+    *reinterpret_cast<float4*>(ws.a + o) = a;
+    *reinterpret_cast<float4*>(ws.bk + o) = bb;
+  }
 }
 
 template <typename E, typename EO, int D>
 __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, DecodeWs ws, int nch) {
   const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = p.Hq / p.Hkv, R = G * p.Tq, Tq = p.Tq, Tk = p.Tk;
-  const int j0 = ch * kCH;
-  __shared__ float sq[kMaxRows][D], sdo[kMaxRows][D];
+  const int j0 = ch * kCH, jn = min(kCH, Tk - j0);
+  __shared__ __attribute__((aligned(16))) float sq[kMaxRows][D];
+  __shared__ __attribute__((aligned(16))) float sdo[kMaxRows][D];
   __shared__ float sP[kMaxRows][kCH], sdS[kMaxRows][kCH];
   __shared__ float sLse[kMaxRows], sDl[kMaxRows];
   const int tid = threadIdx.x;
+
+  // dQ: this workgroup's share of the group's R * D outputs (one per thread when it fits),
+  // summed over chunks in order. Its chunk terms are loaded first, so they arrive while
+  // the statistics merge and dK/dV run.
+  const int total = R * D, per = (total + nch - 1) / nch;
+  const int o0 = ch * per, o1 = min(total, o0 + per);
+  const int64_t rows = (int64_t)p.B * p.Hq * Tq;
+  const bool pre = per <= kThreads && nch <= kPreCh;
+  const int o = o0 + tid;
+  int64_t orow = 0;
+  float pm[kPreCh], pa[kPreCh], pb[kPreCh];
+  if (pre && o < o1) {
+    const int r = o / D, h = kvh * G + r / Tq, i = r % Tq;
+    orow = ((int64_t)b * p.Hq + h) * Tq + i;
+#pragma unroll
+    for (int c = 0; c < kPreCh; ++c) {
+      const int cc = min(c, nch - 1);
+      const int64_t e = ((int64_t)cc * rows + orow) * D + o % D;
+      pm[c] = c < nch ? ws.stats[(orow * nch + cc) * 3] : -INFINITY;
+      pa[c] = ws.a[e];
+      pb[c] = ws.bk[e];
+    }
+  }
 
   // merge every chunk's statistics for each row (16 lanes per row)
   {
@@ -123,18 +239,22 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
       const int h = kvh * G + r / Tq, i = r % Tq;
       const int64_t row = ((int64_t)b * p.Hq + h) * Tq + i;
       const float* st = ws.stats + row * nch * 3;
-      float M = -INFINITY;
-      for (int c = cl; c < nch; c += 16) M = fmaxf(M, st[3 * c]);
-      M = group16_max(M);
-      float L = 0.f, U = 0.f;
+      // one pass per lane (running max with rescaled sums), then across the 16 lanes
+      float M = -INFINITY, L = 0.f, U = 0.f;
       for (int c = cl; c < nch; c += 16) {
-        const float mc = st[3 * c];
-        const float wgt = mc == -INFINITY ? 0.f : expf(mc - M);
-        L += st[3 * c + 1] * wgt;
-        U += st[3 * c + 2] * wgt;
+        const float mc = st[3 * c], lc = st[3 * c + 1], uc = st[3 * c + 2];
+        if (mc == -INFINITY) continue;
+        const float Mn = fmaxf(M, mc);
+        const float wo = expf(M - Mn), wn = expf(mc - Mn);   // M = -inf gives wo = 0
+        L = L * wo + lc * wn;
+        U = U * wo + uc * wn;
+        M = Mn;
       }
-      L = group16_sum(L);
-      U = group16_sum(U);
+      const float Mall = group16_max(M);
+      const float wl = M == -INFINITY ? 0.f : expf(M - Mall);
+      L = group16_sum(L * wl);
+      U = group16_sum(U * wl);
+      M = Mall;
       const float lse = p.lse ? p.lse[row] : M + logf(L);
       if (cl == 0) {
         sLse[r] = lse;
@@ -142,12 +262,7 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
       }
     }
   }
-  for (int idx = tid; idx < R * D; idx += kThreads) {
-    const int r = idx / D, d = idx % D;
-    const int h = kvh * G + r / Tq, i = r % Tq;
-    sq[r][d] = to_f32(rp<E>(p.q, p.sq, b, i, h)[d]);
-    sdo[r][d] = to_f32(rp<E>(p.dout, p.sdo, b, i, h)[d]);
-  }
+  stage_rows<E, D>(p, b, kvh, R, &sq[0][0], &sdo[0][0], D);
   __syncthreads();
   for (int idx = tid; idx < R * kCH; idx += kThreads) {
     const int r = idx / kCH, jj = idx % kCH;
@@ -165,51 +280,66 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
   }
   __syncthreads();
 
-  // dK, dV rows of this chunk: thread owns column d, keys jj = tid / D + k * (256 / D)
+  // dK, dV rows of this chunk: thread owns four columns of one key per pass
   {
-    const int d = tid % D;
-    for (int jj = tid / D; jj < kCH; jj += kThreads / D) {
+    constexpr int C4 = D / 4, KP = kThreads / C4;
+    const int c4 = tid % C4;
+    for (int jj = tid / C4; jj < jn; jj += KP) {
       const int j = j0 + jj;
-      if (j >= Tk) break;
-      float ak = 0.f, av = 0.f;
+      float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
       for (int r = 0; r < R; ++r) {
-        av = fmaf(sP[r][jj], sdo[r][d], av);
-        ak = fmaf(sdS[r][jj], sq[r][d], ak);
+        const float4 qv = *reinterpret_cast<const float4*>(&sq[r][4 * c4]);
+        const float4 ov = *reinterpret_cast<const float4*>(&sdo[r][4 * c4]);
+        const float ps = sP[r][jj], ds = sdS[r][jj];
+        av.x = fmaf(ps, ov.x, av.x); av.y = fmaf(ps, ov.y, av.y); av.z = fmaf(ps, ov.z, av.z); av.w = fmaf(ps, ov.w, av.w);
+        ak.x = fmaf(ds, qv.x, ak.x); ak.y = fmaf(ds, qv.y, ak.y); ak.z = fmaf(ds, qv.z, ak.z); ak.w = fmaf(ds, qv.w, ak.w);
       }
-      EO* dkp = reinterpret_cast<EO*>(p.dk) + (int64_t)b * p.sdk[0] + (int64_t)j * p.sdk[1] + (int64_t)kvh * p.sdk[2];
-      EO* dvp = reinterpret_cast<EO*>(p.dv) + (int64_t)b * p.sdv[0] + (int64_t)j * p.sdv[1] + (int64_t)kvh * p.sdv[2];
-      dkp[d] = from_f32<EO>(ak * p.scale);
-      dvp[d] = from_f32<EO>(av);
+      EO* dkp = reinterpret_cast<EO*>(p.dk) + (int64_t)b * p.sdk[0] + (int64_t)j * p.sdk[1] + (int64_t)kvh * p.sdk[2] + 4 * c4;
+      EO* dvp = reinterpret_cast<EO*>(p.dv) + (int64_t)b * p.sdv[0] + (int64_t)j * p.sdv[1] + (int64_t)kvh * p.sdv[2] + 4 * c4;
+      const float sc = p.scale;
+      if constexpr (std::is_same<EO, float>::value) {
+        *reinterpret_cast<float4*>(dkp) = make_float4(ak.x * sc, ak.y * sc, ak.z * sc, ak.w * sc);
+        *reinterpret_cast<float4*>(dvp) = av;
+      } else {
+        *reinterpret_cast<bf16x4*>(dkp) = bf16x4{(__bf16)(ak.x * sc), (__bf16)(ak.y * sc), (__bf16)(ak.z * sc), (__bf16)(ak.w * sc)};
+        *reinterpret_cast<bf16x4*>(dvp) = bf16x4{(__bf16)av.x, (__bf16)av.y, (__bf16)av.z, (__bf16)av.w};
+      }
     }
   }
-  // dQ partial of this chunk: thread owns column d, rows r = tid / D + k * (256 / D)
-  {
-    const int d = tid % D;
-    const int jn = min(kCH, Tk - j0);
-    for (int r = tid / D; r < R; r += kThreads / D) {
-      const int h = kvh * G + r / Tq, i = r % Tq;
-      float a = 0.f;
-      for (int jj = 0; jj < jn; ++jj) a = fmaf(sdS[r][jj], to_f32(rp<E>(p.k, p.sk, b, j0 + jj, kvh)[d]), a);
-      ws.dq_part[((((int64_t)ch * p.B + b) * p.Hq + h) * Tq + i) * D + d] = a * p.scale;
-    }
-  }
-}
 
-template <typename EO>
-__global__ __launch_bounds__(256) void decode_dq_reduce_kernel(const float* __restrict__ part, int nch, EO* dq,
-                                                               int B, int Hq, int Tq, int D, int64_t s0, int64_t s1,
-                                                               int64_t s2) {
-  const int64_t n = (int64_t)B * Hq * Tq * D;
-  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-    float a = 0.f;
-    for (int c = 0; c < nch; ++c) a += part[(int64_t)c * n + idx];
-    const int d = idx % D;
-    int64_t rest = idx / D;
-    const int i = rest % Tq;
-    rest /= Tq;
-    const int h = rest % Hq;
-    const int b = rest / Hq;
-    dq[b * s0 + i * s1 + h * s2 + d] = from_f32<EO>(a);
+  // dQ_r = scale sum_c exp(m_c - lse_r) (A_c - D_r B_c); D_r B_c is rounded on its own,
+  // so for a single visible key A_c and D_r B_c are the same rounded product and cancel.
+  if (pre) {
+    if (o < o1) {
+      const int r = o / D, h = kvh * G + r / Tq, i = r % Tq;
+      const float lse = sLse[r], Dr = sDl[r];
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kPreCh; ++c) {
+        const float w = pm[c] == -INFINITY ? 0.f : expf(pm[c] - lse);
+        acc += w * (pa[c] - __fmul_rn(Dr, pb[c]));
+      }
+      EO* dqp = reinterpret_cast<EO*>(p.dq) + (int64_t)b * p.sdq[0] + (int64_t)i * p.sdq[1] + (int64_t)h * p.sdq[2];
+      dqp[o % D] = from_f32<EO>(acc * p.scale);
+    }
+  } else {
+    for (int oo = o0 + tid; oo < o1; oo += kThreads) {
+      const int r = oo / D, d = oo % D;
+      const int h = kvh * G + r / Tq, i = r % Tq;
+      const int64_t row = ((int64_t)b * p.Hq + h) * Tq + i;
+      const float lse = sLse[r], Dr = sDl[r];
+      const float* st = ws.stats + row * nch * 3;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < nch; ++c) {
+        const float mc = st[3 * c];
+        const int64_t e = ((int64_t)c * rows + row) * D + d;
+        const float w = mc == -INFINITY ? 0.f : expf(mc - lse);
+        acc += w * (ws.a[e] - __fmul_rn(Dr, ws.bk[e]));
+      }
+      EO* dqp = reinterpret_cast<EO*>(p.dq) + (int64_t)b * p.sdq[0] + (int64_t)i * p.sdq[1] + (int64_t)h * p.sdq[2];
+      dqp[d] = from_f32<EO>(acc * p.scale);
+    }
   }
 }
 
@@ -218,12 +348,10 @@ hipError_t decode_dispatch(const AttnParams& p, void* wsp, hipStream_t s) {
   const int nch = (p.Tk + kCH - 1) / kCH;
   DecodeWs ws = carve(p, wsp);
   const dim3 grid(nch, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_scores_kernel<E, D>), grid, dim3(kThreads), 0, s, p, ws, nch);
+  const int R = (p.Hq / p.Hkv) * p.Tq;
+  const size_t lds = (size_t)(2 * R * D + kCH * (D + 4) + 3 * R * kCH) * sizeof(float);   // <= 62 KB at R = 16
+  hipLaunchKernelGGL((decode_chunk_kernel<E, D>), grid, dim3(kThreads), lds, s, p, ws, nch);
   hipLaunchKernelGGL((decode_grads_kernel<E, EO, D>), grid, dim3(kThreads), 0, s, p, ws, nch);
-  const int64_t n = (int64_t)p.B * p.Hq * p.Tq * D;
-  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL((decode_dq_reduce_kernel<EO>), dim3(blocks), dim3(256), 0, s, ws.dq_part, nch,
-                     reinterpret_cast<EO*>(p.dq), p.B, p.Hq, p.Tq, D, p.sdq[0], p.sdq[1], p.sdq[2]);
   return hipGetLastError();
 }
 
@@ -236,7 +364,7 @@ bool decode_applicable(const AttnParams& p) {
 size_t decode_workspace_bytes(const AttnParams& p) {
   const int64_t nch = (p.Tk + kCH - 1) / kCH;
   const int64_t rows = (int64_t)p.B * p.Hq * p.Tq;
-  const int64_t floats = 2 * align_up(rows * p.Tk) + align_up(rows * nch * 3) + align_up(nch * rows * p.D);
+  const int64_t floats = 2 * align_up(rows * p.Tk) + align_up(rows * nch * 3) + 2 * align_up(nch * rows * p.D);
   return (size_t)floats * sizeof(float);
 }
 
