@@ -232,6 +232,21 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
     }
   }
 
+  // the chunk's stored scores and dP, one (row, key) pair per thread and pass
+  constexpr int kPairs = kMaxRows * kCH / kThreads;
+  float rs[kPairs], rd[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int idx = tid + kThreads * k, r = idx / kCH, j = j0 + idx % kCH;
+    rs[k] = -INFINITY;
+    rd[k] = 0.f;
+    if (r < R && j < Tk) {
+      const int64_t row = ((int64_t)b * p.Hq + kvh * G + r / Tq) * Tq + r % Tq;
+      rs[k] = ws.s[row * Tk + j];
+      rd[k] = ws.dp[row * Tk + j];
+    }
+  }
+
   // merge every chunk's statistics for each row (16 lanes per row)
   {
     const int r = tid >> 4, cl = tid & 15;
@@ -264,19 +279,14 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
   }
   stage_rows<E, D>(p, b, kvh, R, &sq[0][0], &sdo[0][0], D);
   __syncthreads();
-  for (int idx = tid; idx < R * kCH; idx += kThreads) {
-    const int r = idx / kCH, jj = idx % kCH;
-    const int j = j0 + jj;
-    const int h = kvh * G + r / Tq, i = r % Tq;
-    const int64_t row = ((int64_t)b * p.Hq + h) * Tq + i;
-    float pr = 0.f, ds = 0.f;
-    if (j < Tk) {
-      const float s = ws.s[row * Tk + j];
-      pr = s == -INFINITY ? 0.f : expf(s - sLse[r]);
-      ds = pr * (ws.dp[row * Tk + j] - sDl[r]);
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int idx = tid + kThreads * k, r = idx / kCH, jj = idx % kCH;
+    if (r < R) {
+      const float pr = rs[k] == -INFINITY ? 0.f : expf(rs[k] - sLse[r]);
+      sP[r][jj] = pr;
+      sdS[r][jj] = pr * (rd[k] - sDl[r]);
     }
-    sP[r][jj] = pr;
-    sdS[r][jj] = ds;
   }
   __syncthreads();
 
