@@ -16,8 +16,8 @@ the graph's outputs are checked bit for bit against an eager call before timing.
 Prints ONE JSON line. `value` is TFLOP/s of the five contractions the method counts
 (S recompute, dP, dQ, dK, dV) on the exact causal triangle: 10 * d * B * H * T(T+1)/2.
 The roofline object is for the dominant kernel (the longer of the two passes), timed
-live with HIP events that attn_bwd_timed records between the launches of eager steps on
-the launch stream (so a pass's time includes the dispatch gap before it).
+live over the eager steps with HIP events that attn_bwd_timed has the kernel's own
+dispatch record at its start and end, on the launch stream.
 """
 
 from __future__ import annotations
@@ -404,8 +404,8 @@ def main():
         per = {k: [] for k in ("dq", "dkdv")}
         for i in range(nsteps):
             e = phase[4 * i:4 * i + 4]
-            per["dq"].append(hip.ms(e[0], e[1]))
-            per["dkdv"].append(hip.ms(e[1], e[2]))
+            per["dq"].append(hip.ms(e[0], e[1]))             # start/end of each kernel's dispatch
+            per["dkdv"].append(hip.ms(e[2], e[3]))
         hip.destroy(phase + [start, stop])
         return total / nsteps, {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
 

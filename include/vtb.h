@@ -91,12 +91,14 @@ int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void
              const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
-/* attn_bwd with phase timing, for measurement: identical work and results, and the
- * caller's HIP events (hipEvent_t, created by the caller) are recorded on `stream` at
- * the phase boundaries: events[0] before the first launch, then one event after each
- * launch (flash path: query-parallel dq pass, key-parallel dk/dv pass, and events[3]
- * recorded right after events[2]; decode path: chunk statistics, chunk gradients, dQ
- * reduction). n_events must be >= 4. */
+/* attn_bwd with per-kernel timing, for measurement: identical work and results. Every
+ * call runs two kernels on `stream` (flash and MFMA paths: the query-parallel dq pass,
+ * then the key-parallel dk/dv pass; decode path: the chunk pass, then the gradient pass;
+ * Tq == 0: the zero fills of dk and dv), and the caller's HIP events (hipEvent_t,
+ * created by the caller) are recorded by the dispatches themselves: events[0] and
+ * events[1] at the start and end of the first kernel, events[2] and events[3] at the
+ * start and end of the second. A call that launches nothing records none. n_events must
+ * be >= 4. */
 int attn_bwd_timed(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
                    const void* dout, const float* lse, const float* P, void* dq, void* dk,
                    void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream,

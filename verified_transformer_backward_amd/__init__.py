@@ -155,8 +155,9 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dt
              dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
     """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv).
 
-    events: optional sequence of 4 hipEvent_t handles (ints) recorded at the phase
-    boundaries (attn_bwd_timed)."""
+    events: optional sequence of 4 hipEvent_t handles (ints): events[0]/[1] are recorded
+    at the start/end of the call's first kernel, events[2]/[3] of its second
+    (attn_bwd_timed)."""
     out_dtype = out_dtype or q.dtype
     for t, n in ((k, "k"), (v, "v"), (dout, "dout")):
         if t.dtype != q.dtype or t.device != q.device:

@@ -152,15 +152,18 @@ size_t attn_bwd_workspace_size(const attn_bwd_desc* d) {
 
 namespace {
 
-// Records events[i] (when present) on stream s; phase boundaries of attn_bwd.
+// Caller events of attn_bwd_timed: launch i (0 or 1) of a call is timed by events[2i]
+// (its start) and events[2i + 1] (its end).
 struct PhaseEvents {
   void* const* ev;
   int n;
-  int next;
-  int mark(hipStream_t s) {
-    if (!ev || next >= n) return VTB_OK;
-    const hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(ev[next++]), s);
-    return hip_status(e, "hipEventRecord");
+  vtb::KernelEvents pass(int i) const {
+    vtb::KernelEvents k;
+    if (ev && n >= 2 * i + 2) {
+      k.start = reinterpret_cast<hipEvent_t>(ev[2 * i]);
+      k.stop = reinterpret_cast<hipEvent_t>(ev[2 * i + 1]);
+    }
+    return k;
   }
 };
 
@@ -211,21 +214,18 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
 
   if (!has_q) {  // no queries: dK = dV = 0
     if (!has_k) return VTB_OK;
-    rc = hip_status(vtb::launch_zero_bthd(dk, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dk, s), "zero dk");
+    rc = hip_status(vtb::launch_zero_bthd(dk, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dk, s, ev.pass(0)), "zero dk");
     if (rc) return rc;
-    return hip_status(vtb::launch_zero_bthd(dv, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dv, s), "zero dv");
+    return hip_status(vtb::launch_zero_bthd(dv, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dv, s, ev.pass(1)), "zero dv");
   }
 
   const size_t need = attn_bwd_workspace_size(d);
   if (!workspace || workspace_bytes < need)
     return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
 
-  if ((rc = ev.mark(s))) return rc;
   if (!P && vtb::decode_applicable(p)) {
     p.lse = lse;
-    rc = hip_status(vtb::launch_decode(p, workspace, s), "decode path");
-    if (rc) return rc;
-    return ev.mark(s);
+    return hip_status(vtb::launch_decode(p, workspace, s, ev.pass(0), ev.pass(1)), "decode path");
   }
   const FlashWs w = flash_ws(d);
   char* base = reinterpret_cast<char*>(workspace);
@@ -243,16 +243,12 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   }
   const bool mfma = vtb::mfma_path_applicable(p);
   if (mfma && mode == vtb::ROW_LSE_GIVEN)
-    rc = hip_status(vtb::launch_mfma_dq(p, s), "dq pass");
+    rc = hip_status(vtb::launch_mfma_dq(p, s, ev.pass(0)), "dq pass");
   else
-    rc = hip_status(vtb::launch_flash_dq(p, mode, s), "flash dq pass");
-  if (rc || (rc = ev.mark(s))) return rc;
-  if (mfma && !P)
-    rc = hip_status(vtb::launch_mfma_dkdv(p, s), "dk/dv pass");
-  else
-    rc = hip_status(vtb::launch_flash_dkdv(p, s), "flash dk/dv pass");
-  if (rc || (rc = ev.mark(s))) return rc;
-  return ev.mark(s);   // two launches on this path: the last two events coincide
+    rc = hip_status(vtb::launch_flash_dq(p, mode, s, ev.pass(0)), "flash dq pass");
+  if (rc) return rc;
+  if (mfma && !P) return hip_status(vtb::launch_mfma_dkdv(p, s, ev.pass(1)), "dk/dv pass");
+  return hip_status(vtb::launch_flash_dkdv(p, s, ev.pass(1)), "flash dk/dv pass");
 }
 
 }  // namespace
@@ -262,7 +258,7 @@ extern "C" {
 int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
              const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
   return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
-                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0, 0});
+                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0});
 }
 
 int attn_bwd_timed(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout,
@@ -272,7 +268,7 @@ int attn_bwd_timed(const attn_bwd_desc* d, const void* q, const void* k, const v
   for (int i = 0; i < 4; ++i)
     if (!events[i]) return fail(VTB_ERR_ARG, "event %d is NULL", i);
   return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
-                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{events, 4, 0});
+                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{events, 4});
 }
 
 int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* lse, vtb_stream_t stream) {

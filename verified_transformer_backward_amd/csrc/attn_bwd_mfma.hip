@@ -616,17 +616,17 @@ bool mfma_path_applicable(const AttnParams& p) {
   return p.in_bf16 && p.D == kHD && small(p.sq[1]) && small(p.sk[1]) && small(p.sv[1]) && small(p.sdo[1]);
 }
 
-hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s) {
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev) {
   constexpr int BM = kW * 16 * kNT;
   const dim3 grid(p.B * p.Hq, (p.Tq + BM - 1) / BM);
-  hipLaunchKernelGGL(dq_mfma_kernel, grid, dim3(kT), 0, s, p);
+  launch_kernel(dq_mfma_kernel, grid, dim3(kT), 0, s, ev, p);
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s) {
+hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev) {
   constexpr int BN = kW * 16 * kNT;
   const dim3 grid(p.B * p.Hkv, (p.Tk + BN - 1) / BN);
-  hipLaunchKernelGGL(dkdv_mfma_kernel, grid, dim3(kT), 0, s, p);
+  launch_kernel(dkdv_mfma_kernel, grid, dim3(kT), 0, s, ev, p);
   return hipGetLastError();
 }
 

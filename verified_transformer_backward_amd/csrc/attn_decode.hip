@@ -354,14 +354,14 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
 }
 
 template <typename E, typename EO, int D>
-hipError_t decode_dispatch(const AttnParams& p, void* wsp, hipStream_t s) {
+hipError_t decode_dispatch(const AttnParams& p, void* wsp, hipStream_t s, KernelEvents e1, KernelEvents e2) {
   const int nch = (p.Tk + kCH - 1) / kCH;
   DecodeWs ws = carve(p, wsp);
   const dim3 grid(nch, p.Hkv, p.B);
   const int R = (p.Hq / p.Hkv) * p.Tq;
   const size_t lds = (size_t)(2 * R * D + kCH * (D + 4) + 3 * R * kCH) * sizeof(float);   // <= 62 KB at R = 16
-  hipLaunchKernelGGL((decode_chunk_kernel<E, D>), grid, dim3(kThreads), lds, s, p, ws, nch);
-  hipLaunchKernelGGL((decode_grads_kernel<E, EO, D>), grid, dim3(kThreads), 0, s, p, ws, nch);
+  launch_kernel(decode_chunk_kernel<E, D>, grid, dim3(kThreads), (uint32_t)lds, s, e1, p, ws, nch);
+  launch_kernel(decode_grads_kernel<E, EO, D>, grid, dim3(kThreads), 0, s, e2, p, ws, nch);
   return hipGetLastError();
 }
 
@@ -378,13 +378,13 @@ size_t decode_workspace_bytes(const AttnParams& p) {
   return (size_t)floats * sizeof(float);
 }
 
-hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s) {
+hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s, KernelEvents e1, KernelEvents e2) {
   if (p.in_bf16) {
-    if (p.out_bf16) return p.D == 128 ? decode_dispatch<__bf16, __bf16, 128>(p, ws, s) : decode_dispatch<__bf16, __bf16, 64>(p, ws, s);
-    return p.D == 128 ? decode_dispatch<__bf16, float, 128>(p, ws, s) : decode_dispatch<__bf16, float, 64>(p, ws, s);
+    if (p.out_bf16) return p.D == 128 ? decode_dispatch<__bf16, __bf16, 128>(p, ws, s, e1, e2) : decode_dispatch<__bf16, __bf16, 64>(p, ws, s, e1, e2);
+    return p.D == 128 ? decode_dispatch<__bf16, float, 128>(p, ws, s, e1, e2) : decode_dispatch<__bf16, float, 64>(p, ws, s, e1, e2);
   }
-  if (p.out_bf16) return p.D == 128 ? decode_dispatch<float, __bf16, 128>(p, ws, s) : decode_dispatch<float, __bf16, 64>(p, ws, s);
-  return p.D == 128 ? decode_dispatch<float, float, 128>(p, ws, s) : decode_dispatch<float, float, 64>(p, ws, s);
+  if (p.out_bf16) return p.D == 128 ? decode_dispatch<float, __bf16, 128>(p, ws, s, e1, e2) : decode_dispatch<float, __bf16, 64>(p, ws, s, e1, e2);
+  return p.D == 128 ? decode_dispatch<float, float, 128>(p, ws, s, e1, e2) : decode_dispatch<float, float, 64>(p, ws, s, e1, e2);
 }
 
 }  // namespace vtb

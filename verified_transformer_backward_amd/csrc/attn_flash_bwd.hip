@@ -473,39 +473,39 @@ void flash_dkdv_kernel(AttnParams p) {
 }
 
 template <typename E, int D>
-hipError_t dq_dispatch(const AttnParams& p, int mode, hipStream_t s) {
+hipError_t dq_dispatch(const AttnParams& p, int mode, hipStream_t s, KernelEvents ev) {
   const dim3 grid(p.B * p.Hq, (p.Tq + kWaves * 16 - 1) / (kWaves * 16));
   switch (mode) {
-    case ROW_LSE_GIVEN: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
-    case ROW_LSE_COMPUTE: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_COMPUTE>), grid, dim3(kThreads), 0, s, p); break;
-    case ROW_LSE_ONLY: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_LSE_ONLY>), grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((flash_dq_kernel<E, D, ROW_P_GIVEN>), grid, dim3(kThreads), 0, s, p); break;
+    case ROW_LSE_GIVEN: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
+    case ROW_LSE_COMPUTE: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_COMPUTE>, grid, dim3(kThreads), 0, s, ev, p); break;
+    case ROW_LSE_ONLY: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_ONLY>, grid, dim3(kThreads), 0, s, ev, p); break;
+    default: launch_kernel(flash_dq_kernel<E, D, ROW_P_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
   }
   return hipGetLastError();
 }
 
 template <typename E, int D>
-hipError_t dkdv_dispatch(const AttnParams& p, hipStream_t s) {
+hipError_t dkdv_dispatch(const AttnParams& p, hipStream_t s, KernelEvents ev) {
   constexpr int BN = kWaves * 16;
   // x = (batch, kv-head) so that every head's heaviest (earliest) key block is issued first.
   const dim3 grid(p.B * p.Hkv, (p.Tk + BN - 1) / BN);
   if (p.P)
-    hipLaunchKernelGGL((flash_dkdv_kernel<E, D, true>), grid, dim3(kThreads), 0, s, p);
+    launch_kernel(flash_dkdv_kernel<E, D, true>, grid, dim3(kThreads), 0, s, ev, p);
   else
-    hipLaunchKernelGGL((flash_dkdv_kernel<E, D, false>), grid, dim3(kThreads), 0, s, p);
+    launch_kernel(flash_dkdv_kernel<E, D, false>, grid, dim3(kThreads), 0, s, ev, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s) {
-  if (p.in_bf16) return p.D == 128 ? dq_dispatch<__bf16, 128>(p, mode, s) : dq_dispatch<__bf16, 64>(p, mode, s);
-  return p.D == 128 ? dq_dispatch<float, 128>(p, mode, s) : dq_dispatch<float, 64>(p, mode, s);
+hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s, KernelEvents ev) {
+  if (p.in_bf16) return p.D == 128 ? dq_dispatch<__bf16, 128>(p, mode, s, ev) : dq_dispatch<__bf16, 64>(p, mode, s, ev);
+  return p.D == 128 ? dq_dispatch<float, 128>(p, mode, s, ev) : dq_dispatch<float, 64>(p, mode, s, ev);
 }
 
-hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s) {
-  if (p.in_bf16) return p.D == 128 ? dkdv_dispatch<__bf16, 128>(p, s) : dkdv_dispatch<__bf16, 64>(p, s);
-  return p.D == 128 ? dkdv_dispatch<float, 128>(p, s) : dkdv_dispatch<float, 64>(p, s);
+hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev) {
+  if (p.in_bf16) return p.D == 128 ? dkdv_dispatch<__bf16, 128>(p, s, ev) : dkdv_dispatch<__bf16, 64>(p, s, ev);
+  return p.D == 128 ? dkdv_dispatch<float, 128>(p, s, ev) : dkdv_dispatch<float, 64>(p, s, ev);
 }
 
 }  // namespace vtb

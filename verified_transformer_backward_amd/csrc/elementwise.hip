@@ -375,14 +375,15 @@ hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const int64_t st[3], hipStream_t s) {
+hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const int64_t st[3], hipStream_t s,
+                            KernelEvents ev) {
   const int64_t n = (int64_t)B * T * H * D;
   if (n <= 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(zero_bthd_kernel<__bf16>, dim3(grid_for(n)), dim3(256), 0, s, reinterpret_cast<__bf16*>(x), B, T,
+    launch_kernel(zero_bthd_kernel<__bf16>, dim3(grid_for(n)), dim3(256), 0, s, ev, reinterpret_cast<__bf16*>(x), B, T,
                        H, D, st[0], st[1], st[2]);
   else
-    hipLaunchKernelGGL(zero_bthd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, reinterpret_cast<float*>(x), B, T, H,
+    launch_kernel(zero_bthd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, ev, reinterpret_cast<float*>(x), B, T, H,
                        D, st[0], st[1], st[2]);
   return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 // Everything here is already validated by the caller; launchers only compute grids.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,32 +29,50 @@ struct AttnParams {
   int64_t sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
 };
 
+// Optional timing of one kernel: HIP events that the dispatch itself records at the
+// kernel's start and end (hipExtLaunchKernelGGL), so no separate event packet lies
+// between them. Empty: an ordinary launch.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          KernelEvents ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
+
 // How the query-parallel pass obtains P: from the given lse, by computing lse itself
 // (online max/sum), lse only (no backward), or from a saved softmax P.
 enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3 };
 
 // Flash-style path (any Tq): query-parallel pass (row term D, lse when computed, dQ),
 // then key-parallel pass (dK, dV). The second reads D (and lse) written by the first.
-hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s);
-hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s);
+hipError_t launch_flash_dq(const AttnParams& p, int mode, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 
-// bf16, head dim 128: one wave per SIMD with 32-row MFMA blocks and direct-to-LDS tile
-// loads. The dq pass takes a given lse (single sweep; writes dQ and D); the dk/dv pass
+// bf16, head dim 128: MFMA tiles fed by double-buffered direct-to-LDS loads of 64-row
+// blocks. The dq pass takes a given lse (single sweep; writes dQ and D); the dk/dv pass
 // takes lse and D from the workspace or the caller, like launch_flash_dkdv.
 bool mfma_path_applicable(const AttnParams& p);
-hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s);
-hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s);
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 
-// Decode path (Hq/Hkv * Tq <= 16): split-KV chunk statistics, per-chunk gradients, dQ
-// reduction over chunks. Workspace layout is owned by attn_decode.hip.
+// Decode path (Hq/Hkv * Tq <= 16): a chunk pass (scores, dP, split-KV statistics, dQ
+// pieces; reads K and V once) and a gradient pass (dK, dV, dQ; no K/V reads). Workspace
+// layout is owned by attn_decode.hip.
 size_t decode_workspace_bytes(const AttnParams& p);
 bool decode_applicable(const AttnParams& p);
-hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s, KernelEvents ev_chunk = {},
+                         KernelEvents ev_grads = {});
 
 // Fill `n` floats with zero (graph-capture safe, no hipMemsetAsync).
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s);
 // Zero a strided [B, T, H, D] tensor of fp32 or bf16 elements.
-hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const int64_t st[3], hipStream_t s);
+hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const int64_t st[3], hipStream_t s,
+                            KernelEvents ev = {});
 
 // Elementwise tail.
 hipError_t launch_rope_bwd(const float* dy, float* dx, int n_tok, int n_heads, int head_dim,
