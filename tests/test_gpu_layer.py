@@ -107,6 +107,22 @@ def test_linear_shapes(T, K, N):
     assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
 
 
+def test_linear_repeats_bitwise():
+    """30 calls at the layer-chain shape give one bitwise result: a barrier that does not
+    wait for another wave's LDS stores shows up here as a few wrong 32 x 16 tiles."""
+    need_gpu()
+    say("linear T 256 K 2560 N 2560, 30 repeats")
+    rng = np.random.default_rng(7)
+    x = dev(rng.standard_normal((256, 2560)).astype(np.float32))
+    w = dev((rng.standard_normal((2560, 2560)) * 0.02).astype(np.float32))
+    dy = dev(rng.standard_normal((256, 2560)).astype(np.float32))
+    dx0, dw0 = vtb.linear_bwd(x, w, dy)
+    for _ in range(30):
+        dx, dw = vtb.linear_bwd(x, w, dy)
+        assert torch.equal(dx, dx0) and torch.equal(dw, dw0)
+    torch.cuda.synchronize()
+
+
 _KEYS = {"x": "x", "gamma": "gamma", "W": "w", "o": "o", "q": "q", "K": "k", "V": "v", "P": "P"}
 
 

@@ -367,7 +367,10 @@ int linear_bwd(const float* x, const float* w, const float* dy, float* dx, float
 size_t layer_bwd_workspace_size(const layer_bwd_cfg* c) {
   if (!c || c->T < 1 || c->H < 1 || (c->D != 64 && c->D != 128)) return 0;
   const size_t TC = (size_t)c->T * c->H * c->D;
-  return align256(TC * 4) * 2 + align256((size_t)c->H * c->T * 4);   // dO, dq, row term D
+  const int C = c->H * c->D;
+  // dO, dq, the [H, T, T] dP / dS grid, dX partials of the split contraction
+  return align256(TC * 4) * 2 + align256((size_t)c->H * c->T * c->T * 4) +
+         align256((size_t)vtb::linear_bwd_splits(c->T, C, C) * TC * 4);
 }
 
 int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out, float* dh_in, float* dw, float* dk,
@@ -412,34 +415,17 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   char* base = reinterpret_cast<char*>(workspace);
   float* d_o = reinterpret_cast<float*>(base);
   float* dq = reinterpret_cast<float*>(base + align256(TC));
-  float* dlt = reinterpret_cast<float*>(base + 2 * align256(TC));
+  float* ds = reinterpret_cast<float*>(base + 2 * align256(TC));
+  float* part = reinterpret_cast<float*>(base + 2 * align256(TC) + align256((size_t)H * T * T * 4));
 
   // 1. linear backward: dO = dh_out W^T, dW = o^T dh_out
-  int rc = hip_status(vtb::launch_linear_bwd(sv->o, sv->w, dh_out, d_o, dw, T, C, C, s), "layer linear");
+  int rc = hip_status(vtb::launch_linear_bwd_split(sv->o, sv->w, dh_out, d_o, dw, T, C, C, part, s), "layer linear");
   if (rc) return rc;
-  // 2. attention backward with the saved softmax (fp32; dq = scale dS K into the workspace)
-  vtb::AttnParams p{};
-  p.B = 1;
-  p.Hq = p.Hkv = H;
-  p.Tq = p.Tk = T;
-  p.D = D;
-  p.scale = c->scale;
-  p.causal = c->causal;
-  p.in_bf16 = p.out_bf16 = 0;
-  const int64_t st[3] = {(int64_t)T * C, C, D};
-  for (int i = 0; i < 3; ++i) p.sq[i] = p.sk[i] = p.sv[i] = p.sdo[i] = p.sdq[i] = p.sdk[i] = p.sdv[i] = st[i];
-  p.q = sv->q;
-  p.k = sv->k;
-  p.v = sv->v;
-  p.dout = d_o;
-  p.P = sv->P;
-  p.dq = dq;
-  p.dlt = dlt;
-  p.dk = dk;
-  p.dv = dv;
-  rc = hip_status(vtb::launch_flash_dq(p, vtb::ROW_P_GIVEN, s), "layer attention dq pass");
-  if (rc) return rc;
-  rc = hip_status(vtb::launch_flash_dkdv(p, s), "layer attention dk/dv pass");
+  // 2. attention backward with the saved softmax: dP = dO V^T, dS = P o (dP - D), then
+  //    dq = scale dS K (workspace), dK = scale dS^T Q, dV = P^T dO
+  rc = hip_status(vtb::launch_attn_saved_p_bwd(sv->q, sv->k, sv->v, d_o, sv->P, ds, dq, dk, dv, T, H, D, C, c->scale,
+                                               c->causal, s),
+                  "layer attention");
   if (rc) return rc;
   // 3. dh_in = dh_out + RMSNormBackward(x, gamma, RoPEBackward(dq))
   return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq, 1.0f, sv->x, sv->gamma, dh_out, dh_in, T, H, D, 0,

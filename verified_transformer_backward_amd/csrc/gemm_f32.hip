@@ -12,6 +12,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace vtb {
 namespace {
 
@@ -28,7 +30,16 @@ struct GemmDesc {
   int a_kc;        // 1: A is k-contiguous (ak == 1); 0: m-contiguous (am == 1)
   int b_kc;        // 1: B is k-contiguous (bk == 1); 0: n-contiguous (bn == 1)
   int vec;         // float4 loads are valid along the contiguous dimensions
-};
+  int nsplit;      // the contraction is cut into nsplit chunks of kchunk (a multiple of KT);
+  int kchunk;      // chunk s writes its partial product to C + s * c_split
+  int64_t c_split;
+  int batch;       // independent products of this shape: product i at A + i a_b, B + i b_b, C + i c_b
+  int64_t a_b, b_b, c_b;
+  float alpha;     // C = alpha A B
+  int tri;         // causal structure with key j visible to query i iff j <= i + tri_off:
+  int tri_off;     //   TRI_SCORES: C is a (query, key) score grid; tiles wholly invisible are skipped
+};                 //   TRI_KLE: k is the key of row query m (k <= m + off); TRI_KGE: k is the query of row key m (k >= m - off)
+enum { TRI_NONE = 0, TRI_SCORES = 1, TRI_KLE = 2, TRI_KGE = 3 };
 
 // One operand tile, rows [r0, r0+64) x k [k0, k0+KT) of X(r, k) = X[r*sr + k*sk], held
 // in registers between its global loads and its LDS store (two 16-byte chunks per
@@ -40,7 +51,7 @@ struct OpRegs {
   float4 v[2];
   unsigned valid;   // bit 4e + i: element i of chunk e is inside the matrix
   __device__ __forceinline__ void load(const float* X, int64_t sr, int64_t sk, int kc, int vec, int r0, int k0, int R,
-                                       int K) {
+                                       int K) {   // K: end of the contraction range being read
     const int tid = threadIdx.x;
     valid = 0;
 #pragma unroll
@@ -86,17 +97,29 @@ struct OpRegs {
   }
 };
 
-// Tiles of two GEMMs in one grid: blocks [0, tiles0) compute d0, the rest d1. Per k
-// step: one barrier (step k in LDS, step k-1 retired), the next step's loads issued into
-// registers, this step's MFMAs, then the registers stored into the other LDS buffer.
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, int tiles0) {
+// Tiles of up to three GEMMs in one grid: blocks [0, t0) compute d0, [t0, t0 + t1) d1,
+// the rest d2. A GEMM's tiles are ordered (batch, contraction chunk, m tile, n tile).
+// Per k step: one barrier (step k in LDS, step k-1 retired), the next step's loads
+// issued into registers, this step's MFMAs, then the registers stored into the other LDS
+// buffer.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, GemmDesc d2, int t0, int t1) {
   __shared__ __attribute__((aligned(32))) float sA[2][BMG * LDT];
   __shared__ __attribute__((aligned(32))) float sB[2][BNG * LDT];
-  const bool first = (int)blockIdx.x < tiles0;
-  const GemmDesc& d = first ? d0 : d1;
-  const int tile = first ? blockIdx.x : blockIdx.x - tiles0;
-  const int ntn = (d.N + BNG - 1) / BNG;
+  const int bid = blockIdx.x;
+  const int which = bid < t0 ? 0 : (bid < t0 + t1 ? 1 : 2);
+  const GemmDesc& d = which == 0 ? d0 : (which == 1 ? d1 : d2);
+  const int ntn = (d.N + BNG - 1) / BNG, tiles_mn = ((d.M + BMG - 1) / BMG) * ntn;
+  const int t = bid - (which == 0 ? 0 : (which == 1 ? t0 : t0 + t1));
+  const int bi = t / (tiles_mn * d.nsplit), t2 = t % (tiles_mn * d.nsplit);
+  const int split = t2 / tiles_mn, tile = t2 % tiles_mn;
   const int m0 = (tile / ntn) * BMG, n0 = (tile % ntn) * BNG;
+  if (d.tri == TRI_SCORES && n0 > m0 + BMG - 1 + d.tri_off) return;   // no visible (query, key) pair
+  int kbeg = split * d.kchunk, kend = min(d.K, kbeg + d.kchunk);
+  if (d.tri == TRI_KLE) kend = min(kend, m0 + BMG + d.tri_off);
+  if (d.tri == TRI_KGE) kbeg = max(kbeg, ((m0 - d.tri_off) / KT) * KT);
+  const float* const A = d.A + bi * d.a_b;
+  const float* const Bm = d.B + bi * d.b_b;
+  float* const C = d.C + split * d.c_split + bi * d.c_b;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
   const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
 
@@ -107,17 +130,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1,
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   OpRegs ra, rb;
-  ra.load(d.A, d.am, d.ak, d.a_kc, d.vec, m0, 0, d.M, d.K);
-  rb.load(d.B, d.bn, d.bk, d.b_kc, d.vec, n0, 0, d.N, d.K);
-  ra.store(sA[0], d.a_kc);
-  rb.store(sB[0], d.b_kc);
-  const int nk = (d.K + KT - 1) / KT;
+  const int nk = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  if (nk > 0) {
+    ra.load(A, d.am, d.ak, d.a_kc, d.vec, m0, kbeg, d.M, kend);
+    rb.load(Bm, d.bn, d.bk, d.b_kc, d.vec, n0, kbeg, d.N, kend);
+    ra.store(sA[0], d.a_kc);
+    rb.store(sB[0], d.b_kc);
+  }
   for (int s = 0; s < nk; ++s) {
+    // s_waitcnt lgkmcnt(0): this wave's LDS stores of step s have landed before the
+    // barrier publishes them (written out because the barrier's own fence did not get
+    // this wait onto the loop's back edge in every build)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
     __syncthreads();
     const bool more = s + 1 < nk;
     if (more) {
-      ra.load(d.A, d.am, d.ak, d.a_kc, d.vec, m0, (s + 1) * KT, d.M, d.K);
-      rb.load(d.B, d.bn, d.bk, d.b_kc, d.vec, n0, (s + 1) * KT, d.N, d.K);
+      ra.load(A, d.am, d.ak, d.a_kc, d.vec, m0, kbeg + (s + 1) * KT, d.M, kend);
+      rb.load(Bm, d.bn, d.bk, d.b_kc, d.vec, n0, kbeg + (s + 1) * KT, d.N, kend);
     }
     const float* a_t = sA[s & 1];
     const float* b_t = sB[s & 1];
@@ -143,11 +172,48 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm + 16 * i + 4 * lg + r, n = n0 + wn + 16 * j + lc;
-        if (m < d.M && n < d.N) d.C[(int64_t)m * d.ldc + n] = acc[i][j][r];
+        if (m < d.M && n < d.N) C[(int64_t)m * d.ldc + n] = d.alpha * acc[i][j][r];
       }
 }
 
-int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG - 1) / BNG); }
+int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG - 1) / BNG) * d.nsplit * d.batch; }
+
+// out[i] = sum over s of part[s * n + i], in order s = 0, 1, ... (four elements per lane)
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restrict__ part, int ns, int64_t n4,
+                                                         float4* __restrict__ out) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = part[i];
+    for (int s = 1; s < ns; ++s) {
+      const float4 b = part[s * n4 + i];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    out[i] = a;
+  }
+}
+
+// dX = dY W^T and dW = X^T dY descriptors (whole contraction; see launch_linear_bwd).
+void linear_descs(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K, int N,
+                  GemmDesc& gx, GemmDesc& gw) {
+  // dX(t, k) = sum_n dY(t, n) W(k, n): A = dY (k-contiguous), B(n_c, k_out) = W[k_out*N + n_c]
+  gx = GemmDesc{};
+  gx.A = dy; gx.am = N; gx.ak = 1; gx.a_kc = 1;
+  gx.B = w; gx.bk = 1; gx.bn = N; gx.b_kc = 1;
+  gx.C = dx; gx.ldc = K; gx.M = T; gx.N = K; gx.K = N;
+  gx.vec = (N % 4 == 0);
+  gx.nsplit = 1; gx.kchunk = N; gx.c_split = 0;
+  gx.batch = 1; gx.alpha = 1.f;
+  // dW(k, n) = sum_t X(t, k) dY(t, n): A(k, t) = X[t*K + k] (m-contiguous), B(t, n) = dY[t*N + n] (n-contiguous)
+  gw = GemmDesc{};
+  gw.A = x; gw.am = 1; gw.ak = K; gw.a_kc = 0;
+  gw.B = dy; gw.bk = N; gw.bn = 1; gw.b_kc = 0;
+  gw.C = dw; gw.ldc = N; gw.M = K; gw.N = N; gw.K = T;
+  gw.vec = (K % 4 == 0) && (N % 4 == 0);
+  gw.nsplit = 1; gw.kchunk = T; gw.c_split = 0;
+  gw.batch = 1; gw.alpha = 1.f;
+}
 
 }  // namespace
 
@@ -155,25 +221,117 @@ hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, fl
                              hipStream_t s) {
   // The kernel's clamped loads need every extent, the contraction included, >= 1.
   if (T < 1 || K < 1 || N < 1) return hipErrorInvalidValue;
-  // dX(t, k) = sum_n dY(t, n) W(k, n): A = dY (k-contiguous), B(n_c, k_out) = W[k_out*N + n_c]
-  GemmDesc gx{};
-  gx.A = dy; gx.am = N; gx.ak = 1; gx.a_kc = 1;
-  gx.B = w; gx.bk = 1; gx.bn = N; gx.b_kc = 1;
-  gx.C = dx; gx.ldc = K; gx.M = T; gx.N = K; gx.K = N;
-  gx.vec = (N % 4 == 0);
-  // dW(k, n) = sum_t X(t, k) dY(t, n): A(k, t) = X[t*K + k] (m-contiguous), B(t, n) = dY[t*N + n] (n-contiguous)
-  GemmDesc gw{};
-  gw.A = x; gw.am = 1; gw.ak = K; gw.a_kc = 0;
-  gw.B = dy; gw.bk = N; gw.bn = 1; gw.b_kc = 0;
-  gw.C = dw; gw.ldc = N; gw.M = K; gw.N = N; gw.K = T;
-  gw.vec = (K % 4 == 0) && (N % 4 == 0);
+  GemmDesc gx, gw;
+  linear_descs(x, w, dy, dx, dw, T, K, N, gx, gw);
   const int tx = dx ? tiles_of(gx) : 0;
   const int tw = dw ? tiles_of(gw) : 0;
   if (tx + tw == 0) return hipSuccess;
   if (tx)
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, tx);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
   else
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tw), dim3(256), 0, s, gw, gw, tw);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tw), dim3(256), 0, s, gw, gw, gw, tw, 0);
+  return hipGetLastError();
+}
+
+int linear_bwd_splits(int T, int K, int N) {
+  (void)T;
+  (void)K;
+  const int nk = (N + KT - 1) / KT;   // k steps of dX's contraction
+  const int want = std::max(1, std::min(8, nk / 16));
+  const int per = (nk + want - 1) / want;
+  return (nk + per - 1) / per;        // every chunk non-empty
+}
+
+hipError_t launch_linear_bwd_split(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K,
+                                   int N, float* part, hipStream_t s) {
+  if (T < 1 || K < 1 || N < 1 || !dx || !dw) return hipErrorInvalidValue;
+  const int ns = linear_bwd_splits(T, K, N);
+  if (ns == 1 || ((int64_t)T * K) % 4) return launch_linear_bwd(x, w, dy, dx, dw, T, K, N, s);
+  GemmDesc gx, gw;
+  linear_descs(x, w, dy, part, dw, T, K, N, gx, gw);
+  const int nk = (N + KT - 1) / KT;
+  gx.nsplit = ns;
+  gx.kchunk = ((nk + ns - 1) / ns) * KT;
+  gx.c_split = (int64_t)T * K;
+  const int tx = tiles_of(gx), tw = tiles_of(gw);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
+  const int64_t n4 = (int64_t)T * K / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(part), ns, n4,
+                     reinterpret_cast<float4*>(dx));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ attention with a saved P
+namespace {
+
+// D_i = sum_j P_ij dP_ij over the visible keys and dS_ij = P_ij (dP_ij - D_i) (zero where
+// invisible), in place over dP; one wave per (head, query) row of the [H, T, T] grid.
+__global__ __launch_bounds__(256) void softmax_bwd_rows_kernel(const float* __restrict__ P, float* __restrict__ ds,
+                                                               int rows, int T, int causal) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int i = r % T, lim = causal ? i : T - 1;
+  const float* pr = P + (int64_t)r * T;
+  float* dr = ds + (int64_t)r * T;
+  float acc = 0.f;
+  for (int j = lane; j <= lim; j += 64) acc = fmaf(pr[j], dr[j], acc);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  for (int j = lane; j < T; j += 64) dr[j] = j <= lim ? pr[j] * (dr[j] - acc) : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
+                                   float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld, float scale,
+                                   int causal, hipStream_t s) {
+  if (T < 1 || H < 1 || D < 1 || ld < H * D) return hipErrorInvalidValue;
+  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld % 4 == 0;
+  auto base = [&](GemmDesc& g) {
+    g = GemmDesc{};
+    g.nsplit = 1;
+    g.c_split = 0;
+    g.batch = H;
+    g.alpha = 1.f;
+    g.vec = v4;
+  };
+  // dP = dO V^T per head, on the (query, key) tiles that hold a visible pair
+  GemmDesc gp;
+  base(gp);
+  gp.A = dout; gp.am = ld; gp.ak = 1; gp.a_kc = 1; gp.a_b = D;
+  gp.B = v; gp.bk = 1; gp.bn = ld; gp.b_kc = 1; gp.b_b = D;
+  gp.C = ds; gp.ldc = T; gp.c_b = (int64_t)T * T;
+  gp.M = T; gp.N = T; gp.K = D; gp.kchunk = D;
+  gp.tri = causal ? TRI_SCORES : TRI_NONE;
+  const int tp = tiles_of(gp);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(tp), dim3(256), 0, s, gp, gp, gp, tp, 0);
+  const int rows = H * T;
+  hipLaunchKernelGGL(softmax_bwd_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, P, ds, rows, T, causal);
+  // dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO per head, contraction limited to the
+  // visible keys (dQ) or queries (dK, dV)
+  GemmDesc gq, gk, gv;
+  base(gq);
+  gq.A = ds; gq.am = T; gq.ak = 1; gq.a_kc = 1; gq.a_b = (int64_t)T * T;
+  gq.B = k; gq.bk = ld; gq.bn = 1; gq.b_kc = 0; gq.b_b = D;
+  gq.C = dq; gq.ldc = ld; gq.c_b = D;
+  gq.M = T; gq.N = D; gq.K = T; gq.kchunk = T;
+  gq.alpha = scale;
+  gq.tri = causal ? TRI_KLE : TRI_NONE;
+  base(gk);
+  gk.A = ds; gk.am = 1; gk.ak = T; gk.a_kc = 0; gk.a_b = (int64_t)T * T;
+  gk.B = q; gk.bk = ld; gk.bn = 1; gk.b_kc = 0; gk.b_b = D;
+  gk.C = dk; gk.ldc = ld; gk.c_b = D;
+  gk.M = T; gk.N = D; gk.K = T; gk.kchunk = T;
+  gk.alpha = scale;
+  gk.tri = causal ? TRI_KGE : TRI_NONE;
+  gv = gk;
+  gv.A = P;
+  gv.B = dout;
+  gv.C = dv;
+  gv.alpha = 1.f;
+  const int t0 = tiles_of(gq), t1 = tiles_of(gk), t2 = tiles_of(gv);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(t0 + t1 + t2), dim3(256), 0, s, gq, gk, gv, t0, t1);
   return hipGetLastError();
 }
 

@@ -88,5 +88,19 @@ hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const fl
 // fp32 MFMA GEMMs of the linear backward (one launch computes both products).
 hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw,
                              int T, int K, int N, hipStream_t s);
+// The same products with dX's contraction cut into linear_bwd_splits(T, K, N) chunks that
+// run as separate tiles (their fp32 partials in `part`, splits * T * K floats, 16-byte
+// aligned), then summed into dx in chunk order. For the layer chain, where dX's 2560-deep
+// contraction would otherwise be the critical path. dx and dw are both required.
+int linear_bwd_splits(int T, int K, int N);
+// Attention backward with a saved softmax, as batched fp32 MFMA GEMMs over H heads of a
+// [T, ld] activation layout (head h at column h * D; B = 1, Tq = Tk = T): dP = dO V^T into
+// ds [H, T, T], dS = P o (dP - D) in place, then dQ = scale dS K, dK = scale dS^T Q and
+// dV = P^T dO in one launch. Causal tiles and contraction ranges skip invisible pairs.
+hipError_t launch_linear_bwd_split(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K,
+                                   int N, float* part, hipStream_t s);
+hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
+                                   float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld, float scale,
+                                   int causal, hipStream_t s);
 
 }  // namespace vtb
