@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-baseline sample time")
     ap.add_argument("--no-extra", action="store_true", help="skip the other hot-path workloads")
+    ap.add_argument("--only", default="", help="run only these other workloads (comma list, e.g. layer_chain) "
+                                               "and print their results; no headline step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling profiler byte counters)")
     return ap.parse_args()
@@ -150,129 +152,141 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-def extra_workloads(torch, vtb, hip):
+EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain")
+
+
+def extra_workloads(torch, vtb, hip, only=None):
     """The other rows of the hot path at their workload sizes, each against its roofline.
     Inputs are seeded synthetic tensors; the layer chain's saved activations come from a
-    plain torch fp32 forward of each layer (setup only, untimed)."""
+    plain torch fp32 forward of each layer (setup only, untimed). `only`: names to run."""
     import numpy as np
     import synth
 
     dev = torch.device("cuda:0")
     out = {}
+    H, d = 20, 128
+    C = H * d
+
+    def want(name):
+        return only is None or name in only
 
     def up(a, dtype="f32"):
         if dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(synth.bf16_bits(a))).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
-    # decode-shaped GQA: B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, no lse (HBM-bound: K, V in, dK, dV out)
-    x = synth.decode_gqa_inputs()
-    t = {n: up(x[n]) for n in ("q", "k", "v", "dout")}
-    o = {n: torch.empty_like(t[n]) for n in ("q", "k", "v")}
-    desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], False, torch.float32, t["dout"], o["q"], o["k"], o["v"], t["v"])
-    ws = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
-    f = lambda: vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], False, dq=o["q"], dk=o["k"], dv=o["v"],
-                             workspace=ws, stream=torch.cuda.current_stream())
-    ms = graph_ms(torch, hip, f, 50)
-    byts = sum(v.numel() * 4 for v in t.values()) + sum(v.numel() * 4 for v in o.values())
-    out["decode_gqa"] = {"workload": "GQA decode B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, lse computed", "ms": round(ms, 5),
-                         "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                         "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "algorithmic_bytes": byts}}
-    del t, o, ws
+    if want("decode_gqa"):
+        # decode-shaped GQA: B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, no lse (HBM-bound: K, V in, dK, dV out)
+        x = synth.decode_gqa_inputs()
+        t = {n: up(x[n]) for n in ("q", "k", "v", "dout")}
+        o = {n: torch.empty_like(t[n]) for n in ("q", "k", "v")}
+        desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], False, torch.float32, t["dout"], o["q"], o["k"], o["v"], t["v"])
+        ws = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+        f = lambda: vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], False, dq=o["q"], dk=o["k"], dv=o["v"],
+                                 workspace=ws, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 50)
+        byts = sum(v.numel() * 4 for v in t.values()) + sum(v.numel() * 4 for v in o.values())
+        out["decode_gqa"] = {"workload": "GQA decode B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, lse computed", "ms": round(ms, 5),
+                             "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                             "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                          "algorithmic_bytes": byts}}
+        del t, o, ws
 
-    # long-context causal: B1 H32 T8192 d128 bf16, lse given (bf16 MFMA-bound)
-    x = synth.long_causal_inputs()
-    t = {n: up(x[n], "bf16") for n in ("q", "k", "v", "dout")}
-    lse = vtb.attn_fwd_lse(t["q"], t["k"], x["scale"], True)
-    o = {n: torch.empty_like(t[n]) for n in ("q", "k", "v")}
-    desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], True, torch.bfloat16, t["dout"], o["q"], o["k"], o["v"], t["v"])
-    ws = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
-    f = lambda: vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], True, lse=lse, dq=o["q"], dk=o["k"],
-                             dv=o["v"], workspace=ws, stream=torch.cuda.current_stream())
-    ms = graph_ms(torch, hip, f, 5)
-    fl = 10 * 128 * 32 * 8192 * 8193 // 2
-    out["long_causal"] = {"workload": "causal B1 H32 T8192 d128 bf16, lse given", "ms": round(ms, 4),
-                          "value": round(fl / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
-                          "roofline": {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                                       "algorithmic_flops": fl}}
-    del t, o, ws, lse
+    if want("long_causal"):
+        # long-context causal: B1 H32 T8192 d128 bf16, lse given (bf16 MFMA-bound)
+        x = synth.long_causal_inputs()
+        t = {n: up(x[n], "bf16") for n in ("q", "k", "v", "dout")}
+        lse = vtb.attn_fwd_lse(t["q"], t["k"], x["scale"], True)
+        o = {n: torch.empty_like(t[n]) for n in ("q", "k", "v")}
+        desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], True, torch.bfloat16, t["dout"], o["q"], o["k"], o["v"], t["v"])
+        ws = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+        f = lambda: vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], True, lse=lse, dq=o["q"], dk=o["k"],
+                                 dv=o["v"], workspace=ws, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 5)
+        fl = 10 * 128 * 32 * 8192 * 8193 // 2
+        out["long_causal"] = {"workload": "causal B1 H32 T8192 d128 bf16, lse given", "ms": round(ms, 4),
+                              "value": round(fl / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                              "roofline": {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                           "algorithmic_flops": fl}}
+        del t, o, ws, lse
 
-    # fused RoPE -> RMSNorm -> residual tail on the stack shape (30 x 256 rows, hidden 2560), fp32
-    rows, H, d = 30 * 256, 20, 128
-    C = H * d
-    rng = np.random.default_rng(1007)
-    dq_, xx, dh = (torch.from_numpy(rng.standard_normal((rows, C)).astype(np.float32)).to(dev) for _ in range(3))
-    gam = torch.from_numpy(rng.uniform(0.5, 1.5, C).astype(np.float32)).to(dev)
-    dh_in = torch.empty_like(dh)
-    f = lambda: vtb.rope_rmsnorm_res_bwd(dq_, xx, gam, dh, H, d, dh_in=dh_in, stream=torch.cuda.current_stream())
-    ms = graph_ms(torch, hip, f, 20)
-    byts = 4 * rows * C * 4
-    out["rope_rmsnorm_res"] = {"workload": "fused RoPE+RMSNorm+residual backward, 7680 x 2560 fp32", "ms": round(ms, 5),
-                               "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                               "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                            "algorithmic_bytes": byts}}
-    dy3 = dq_.view(rows, H, d)
-    dx3 = torch.empty_like(dy3)
-    f = lambda: vtb.rope_bwd(dy3, dx=dx3, stream=torch.cuda.current_stream())
-    ms = graph_ms(torch, hip, f, 20)
-    byts = 2 * rows * C * 4
-    out["rope_bwd"] = {"workload": "RoPE backward, 7680 x 20 x 128 fp32", "ms": round(ms, 5),
-                       "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                       "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "algorithmic_bytes": byts}}
-    f = lambda: vtb.rmsnorm_bwd(xx, gam, dh, dx=dh_in, stream=torch.cuda.current_stream())
-    ms = graph_ms(torch, hip, f, 20)
-    byts = 3 * rows * C * 4
-    out["rmsnorm_bwd"] = {"workload": "RMSNorm backward, 7680 x 2560 fp32", "ms": round(ms, 5),
-                          "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                          "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                       "algorithmic_bytes": byts}}
-    del dq_, xx, dh, dh_in, dy3, dx3
+    if want("rope_rmsnorm_res") or want("rope_bwd") or want("rmsnorm_bwd"):
+        # fused RoPE -> RMSNorm -> residual tail on the stack shape (30 x 256 rows, hidden 2560), fp32
+        rows, H, d = 30 * 256, 20, 128
+        C = H * d
+        rng = np.random.default_rng(1007)
+        dq_, xx, dh = (torch.from_numpy(rng.standard_normal((rows, C)).astype(np.float32)).to(dev) for _ in range(3))
+        gam = torch.from_numpy(rng.uniform(0.5, 1.5, C).astype(np.float32)).to(dev)
+        dh_in = torch.empty_like(dh)
+        f = lambda: vtb.rope_rmsnorm_res_bwd(dq_, xx, gam, dh, H, d, dh_in=dh_in, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        byts = 4 * rows * C * 4
+        out["rope_rmsnorm_res"] = {"workload": "fused RoPE+RMSNorm+residual backward, 7680 x 2560 fp32", "ms": round(ms, 5),
+                                   "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                   "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                                "algorithmic_bytes": byts}}
+        dy3 = dq_.view(rows, H, d)
+        dx3 = torch.empty_like(dy3)
+        f = lambda: vtb.rope_bwd(dy3, dx=dx3, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        byts = 2 * rows * C * 4
+        out["rope_bwd"] = {"workload": "RoPE backward, 7680 x 20 x 128 fp32", "ms": round(ms, 5),
+                           "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                           "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "algorithmic_bytes": byts}}
+        f = lambda: vtb.rmsnorm_bwd(xx, gam, dh, dx=dh_in, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        byts = 3 * rows * C * 4
+        out["rmsnorm_bwd"] = {"workload": "RMSNorm backward, 7680 x 2560 fp32", "ms": round(ms, 5),
+                              "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                           "algorithmic_bytes": byts}}
+        del dq_, xx, dh, dh_in, dy3, dx3
 
-    # 30-layer chain: T256, hidden 2560 = 20 x 128, fp32, saved softmax P per layer
-    L, T = 30, 256
-    sc = 1.0 / np.sqrt(d)
-    pos = torch.arange(T, device=dev, dtype=torch.float64)
-    inv = 10000.0 ** (-2.0 * torch.arange(d // 2, device=dev, dtype=torch.float64) / d)
-    ang = pos[:, None] * inv[None, :]
-    cos, sin = torch.cos(ang).float()[:, None, :], torch.sin(ang).float()[:, None, :]
-    mask = torch.tril(torch.ones(T, T, dtype=torch.bool, device=dev))
-    saved = []
-    for l in range(L):
-        li = synth.layer_inputs(l, T, H, d)
-        h, K, V, W, gm = (up(li[n]) for n in ("h", "K", "V", "W", "gamma"))
-        xn = h * torch.rsqrt((h * h).mean(1, keepdim=True) + 1e-6) * gm
-        xr = xn.view(T, H, d)
-        a, b2 = xr[..., 0::2], xr[..., 1::2]
-        q = torch.stack((a * cos - b2 * sin, a * sin + b2 * cos), -1).reshape(T, H, d).contiguous()
-        S = torch.matmul(q.permute(1, 0, 2).contiguous(), K.permute(1, 2, 0).contiguous()) * sc
-        P = torch.softmax(S.masked_fill(~mask, float("-inf")), -1).contiguous()
-        ob = torch.matmul(P, V.permute(1, 0, 2).contiguous()).permute(1, 0, 2).reshape(T, C).contiguous()
-        saved.append({"x": h, "gamma": gm, "w": W, "o": ob, "q": q, "k": K.contiguous(), "v": V.contiguous(), "P": P})
-    g0 = up(synth.layer_upstream_grad(T, H, d))
-    gs = [torch.empty_like(g0) for _ in range(L)]
-    dws = [torch.empty_like(saved[0]["w"]) for _ in range(L)]
-    dks = [torch.empty_like(saved[0]["k"]) for _ in range(L)]
-    dvs = [torch.empty_like(saved[0]["v"]) for _ in range(L)]
-    cfg = vtb.make_layer_cfg(T, H, d, sc)
-    lws = torch.empty(vtb.layer_bwd_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    if want("layer_chain"):
+        # 30-layer chain: T256, hidden 2560 = 20 x 128, fp32, saved softmax P per layer
+        L, T = 30, 256
+        sc = 1.0 / np.sqrt(d)
+        pos = torch.arange(T, device=dev, dtype=torch.float64)
+        inv = 10000.0 ** (-2.0 * torch.arange(d // 2, device=dev, dtype=torch.float64) / d)
+        ang = pos[:, None] * inv[None, :]
+        cos, sin = torch.cos(ang).float()[:, None, :], torch.sin(ang).float()[:, None, :]
+        mask = torch.tril(torch.ones(T, T, dtype=torch.bool, device=dev))
+        saved = []
+        for l in range(L):
+            li = synth.layer_inputs(l, T, H, d)
+            h, K, V, W, gm = (up(li[n]) for n in ("h", "K", "V", "W", "gamma"))
+            xn = h * torch.rsqrt((h * h).mean(1, keepdim=True) + 1e-6) * gm
+            xr = xn.view(T, H, d)
+            a, b2 = xr[..., 0::2], xr[..., 1::2]
+            q = torch.stack((a * cos - b2 * sin, a * sin + b2 * cos), -1).reshape(T, H, d).contiguous()
+            S = torch.matmul(q.permute(1, 0, 2).contiguous(), K.permute(1, 2, 0).contiguous()) * sc
+            P = torch.softmax(S.masked_fill(~mask, float("-inf")), -1).contiguous()
+            ob = torch.matmul(P, V.permute(1, 0, 2).contiguous()).permute(1, 0, 2).reshape(T, C).contiguous()
+            saved.append({"x": h, "gamma": gm, "w": W, "o": ob, "q": q, "k": K.contiguous(), "v": V.contiguous(), "P": P})
+        g0 = up(synth.layer_upstream_grad(T, H, d))
+        gs = [torch.empty_like(g0) for _ in range(L)]
+        dws = [torch.empty_like(saved[0]["w"]) for _ in range(L)]
+        dks = [torch.empty_like(saved[0]["k"]) for _ in range(L)]
+        dvs = [torch.empty_like(saved[0]["v"]) for _ in range(L)]
+        cfg = vtb.make_layer_cfg(T, H, d, sc)
+        lws = torch.empty(vtb.layer_bwd_workspace_size(cfg), dtype=torch.uint8, device=dev)
 
-    def chain():
-        g = g0
-        for l in reversed(range(L)):
-            vtb.layer_bwd(saved[l], g, sc, dh_in=gs[l], dw=dws[l], dk=dks[l], dv=dvs[l], workspace=lws,
-                          stream=torch.cuda.current_stream())
-            g = gs[l]
+        def chain():
+            g = g0
+            for l in reversed(range(L)):
+                vtb.layer_bwd(saved[l], g, sc, dh_in=gs[l], dw=dws[l], dk=dks[l], dv=dvs[l], workspace=lws,
+                              stream=torch.cuda.current_stream())
+                g = gs[l]
 
-    ms = graph_ms(torch, hip, chain, 3)
-    pairs = H * T * (T + 1) // 2
-    fl = L * (4 * T * C * C + 8 * d * pairs)
-    out["layer_chain"] = {"workload": "30-layer backward chain, T256 hidden 2560 (20 x 128) fp32, saved P",
-                          "ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                          "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
-                                       "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
-                                       "algorithmic_flops": fl}}
+        ms = graph_ms(torch, hip, chain, 3)
+        pairs = H * T * (T + 1) // 2
+        fl = L * (4 * T * C * C + 8 * d * pairs)
+        out["layer_chain"] = {"workload": "30-layer backward chain, T256 hidden 2560 (20 x 128) fp32, saved P",
+                              "ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
+                                           "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                                           "algorithmic_flops": fl}}
     return out
 
 
@@ -323,6 +337,20 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.only:                                         # one or more of the other workloads alone (profiling)
+        names = [n for n in args.only.split(",") if n]
+        bad = [n for n in names if n not in EXTRA_NAMES]
+        if bad:
+            print(f"bench.py: unknown workload(s) {bad}; choose from {list(EXTRA_NAMES)}", file=sys.stderr)
+            return 2
+        torch.cuda.init()
+        if args.calibrate_copy:   # same known-size copy as the headline run
+            src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda:0")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        print(json.dumps({"only": names, "other_workloads": extra_workloads(torch, vtb, HipEvents(), set(names))}))
+        return 0
     B, T, H, d = 4, 512, 20, 128
     x = synth.causal_inputs(B, T, H, d)
     sc = float(x["scale"])
