@@ -134,6 +134,10 @@ CASES = [
     ("bf16_decode_Tq1_d64", 2, 1, 257, 4, 4, 64, "bf16", False),
     ("bf16_single_key", 1, 1, 1, 2, 2, 64, "bf16", True),
     ("f32_causal_T33", 1, 33, 33, 1, 1, 64, "f32", True),
+    # bf16 d 128 MFMA passes: GQA with Tq < Tk on whole blocks, no mask, a 32-row last block
+    ("bf16_causal_gqa_Tq64_Tk160", 2, 64, 160, 8, 2, 128, "bf16", True),
+    ("bf16_noncausal_T96", 1, 96, 96, 4, 4, 128, "bf16", False),
+    ("bf16_causal_T224", 2, 224, 224, 3, 3, 128, "bf16", True),
 ]
 
 
@@ -150,6 +154,29 @@ def test_edge_shapes(case):
     _check(name, got, ref, TOL[dtype], floors)
     got2 = _run(x, dtype, sc, causal, lse=None)        # lse computed inside
     _check(name + "_nolse", got2, ref, TOL[dtype], floors)
+
+
+def test_consecutive_calls_share_workspace():
+    """Two different problems through one workspace, back to back, three times: the row
+    term D that the second pass reads must be the current call's."""
+    say("bf16 causal B2 T256 H4 d128, two inputs, one workspace")
+    sc = 1.0 / np.sqrt(128)
+    xs = [synth.attention_inputs(2, 256, 256, 4, 4, 128, "bf16", seed=s) for s in (501, 502)]
+    ts = [{n: dev(x[n], "bf16") for n in ("q", "k", "v", "dout")} for x in xs]
+    lses = [torch.from_numpy(A.attention_lse(x["q"], x["k"], sc, True).astype(np.float32)).cuda() for x in xs]
+    desc = vtb.make_attn_desc(ts[0]["q"], ts[0]["k"], sc, True, torch.bfloat16, ts[0]["dout"], ts[0]["q"], ts[0]["k"],
+                              ts[0]["v"], ts[0]["v"])
+    ws = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for rep in range(3):
+        for t, lse in zip(ts, lses):
+            outs.append(vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, True, lse=lse, workspace=ws))
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        lse = A.attention_lse(x["q"], x["k"], sc, True).astype(np.float32)
+        ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, True, lse=lse)
+        for rep in range(3):
+            _check(f"consecutive_{i}_{rep}", [host(a) for a in outs[2 * rep + i]], ref, TOL["bf16"], (0.0, 0.0, 0.0))
 
 
 def test_strided_head_major_layout():
