@@ -13,6 +13,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace vtb {
 namespace {
@@ -43,32 +44,59 @@ enum { TRI_NONE = 0, TRI_SCORES = 1, TRI_KLE = 2, TRI_KGE = 3 };
 
 // One operand tile, rows [r0, r0+64) x k [k0, k0+KT) of X(r, k) = X[r*sr + k*sk], held
 // in registers between its global loads and its LDS store (two 16-byte chunks per
-// thread). load() issues every load at once, always in bounds (indices clamped, an
-// element outside the matrix is zeroed by store()), so the loads of the next k step
-// run under the current step's MFMAs. store() writes tile[r][k] (k-contiguous rows),
-// transposing when X is r-contiguous.
-struct OpRegs {
+// thread). KC: 1 when X is k-contiguous (64 rows x 8 chunks of 4 k), 0 when r-contiguous
+// (KT k x 16 chunks of 4 rows). store() writes tile[r][k] (k-contiguous rows),
+// transposing when KC == 0.
+//
+// OpEdge serves tiles that reach past an edge of the matrix: every load is clamped in
+// bounds and the elements outside are zeroed by store(). OpInner serves tiles wholly
+// inside: the two chunk addresses are computed once and advanced by one k step per load.
+template <int KC>
+__device__ __forceinline__ void chunk_of(int idx, int& r, int& k) {
+  r = KC ? (idx >> 3) : (idx & 15) * 4;
+  k = KC ? (idx & 7) * 4 : (idx >> 4);
+}
+
+template <int KC>
+__device__ __forceinline__ void store_chunks(float* tile, const float4 (&v)[2]) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    int r, k;
+    chunk_of<KC>(threadIdx.x + 256 * e, r, k);
+    if (KC) {
+      *reinterpret_cast<float4*>(tile + r * LDT + k) = v[e];
+    } else {
+      tile[(r + 0) * LDT + k] = v[e].x;
+      tile[(r + 1) * LDT + k] = v[e].y;
+      tile[(r + 2) * LDT + k] = v[e].z;
+      tile[(r + 3) * LDT + k] = v[e].w;
+    }
+  }
+}
+
+template <int KC>
+struct OpEdge {
+  const float* X;
+  int64_t sr, sk;
+  int r0, R, K, vec;   // K: end of the contraction range being read
   float4 v[2];
-  unsigned valid;   // bit 4e + i: element i of chunk e is inside the matrix
-  __device__ __forceinline__ void load(const float* X, int64_t sr, int64_t sk, int kc, int vec, int r0, int k0, int R,
-                                       int K) {   // K: end of the contraction range being read
-    const int tid = threadIdx.x;
+  unsigned valid;      // bit 4e + i: element i of chunk e is inside the matrix
+  __device__ __forceinline__ void load(int k0) {
     valid = 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;
-      // kc: 64 rows x 8 chunks of 4 k;  !kc: KT k x 16 chunks of 4 rows
-      const int gr = kc ? r0 + (idx >> 3) : r0 + (idx & 15) * 4;
-      const int gk = kc ? k0 + (idx & 7) * 4 : k0 + (idx >> 4);
+      int r, k;
+      chunk_of<KC>(threadIdx.x + 256 * e, r, k);
+      const int gr = r0 + r, gk = k0 + k;
       if (vec) {
-        const int cr = min(gr, R - (kc ? 1 : 4)), ck = min(gk, K - (kc ? 4 : 1));
+        const int cr = min(gr, R - (KC ? 1 : 4)), ck = min(gk, K - (KC ? 4 : 1));
         v[e] = *reinterpret_cast<const float4*>(X + (int64_t)cr * sr + (int64_t)ck * sk);
         if (gr < R && gk < K) valid |= 0xFu << (4 * e);
       } else {
         float t[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = kc ? gr : gr + i, kk = kc ? gk + i : gk;
+          const int rr = KC ? gr : gr + i, kk = KC ? gk + i : gk;
           t[i] = X[(int64_t)min(rr, R - 1) * sr + (int64_t)min(kk, K - 1) * sk];
           if (rr < R && kk < K) valid |= 1u << (4 * e + i);
         }
@@ -76,32 +104,118 @@ struct OpRegs {
       }
     }
   }
-  __device__ __forceinline__ void store(float* tile, int kc) const {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void store(float* tile) const {
+    float4 x[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;
       const unsigned m = valid >> (4 * e);
-      const float4 x = make_float4(m & 1u ? v[e].x : 0.f, m & 2u ? v[e].y : 0.f, m & 4u ? v[e].z : 0.f,
-                                   m & 8u ? v[e].w : 0.f);
-      if (kc) {
-        *reinterpret_cast<float4*>(tile + (idx >> 3) * LDT + (idx & 7) * 4) = x;
-      } else {
-        const int k = idx >> 4, rq = (idx & 15) * 4;
-        tile[(rq + 0) * LDT + k] = x.x;
-        tile[(rq + 1) * LDT + k] = x.y;
-        tile[(rq + 2) * LDT + k] = x.z;
-        tile[(rq + 3) * LDT + k] = x.w;
-      }
+      x[e] = make_float4(m & 1u ? v[e].x : 0.f, m & 2u ? v[e].y : 0.f, m & 4u ? v[e].z : 0.f, m & 8u ? v[e].w : 0.f);
     }
+    store_chunks<KC>(tile, x);
   }
 };
 
+template <int KC>
+struct OpInner {
+  const float* p[2];   // the thread's two chunks at the next k step
+  int64_t step;        // elements between k steps
+  float4 v[2];
+  __device__ __forceinline__ void init(const float* X, int64_t sr, int64_t sk, int r0, int k0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      int r, k;
+      chunk_of<KC>(threadIdx.x + 256 * e, r, k);
+      p[e] = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
+    }
+    step = (int64_t)KT * sk;
+  }
+  __device__ __forceinline__ void load() {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      v[e] = *reinterpret_cast<const float4*>(p[e]);
+      p[e] += step;
+    }
+  }
+  __device__ __forceinline__ void store(float* tile) const { store_chunks<KC>(tile, v); }
+};
+
+// One 64 x 64 tile of C = alpha A B over k in [kbeg, kend). Per k step: one barrier (step k
+// in LDS, step k-1 retired), the next step's loads issued into registers, this step's
+// MFMAs, then the registers stored into the other LDS buffer.
+template <bool INNER, int AKC, int BKC>
+__device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, const float* Bm, float* C, int m0, int n0,
+                                          int kbeg, int kend, float (*sA)[BMG * LDT], float (*sB)[BNG * LDT]) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  typename std::conditional<INNER, OpInner<AKC>, OpEdge<AKC>>::type ra;
+  typename std::conditional<INNER, OpInner<BKC>, OpEdge<BKC>>::type rb;
+  auto load = [&](int k0) {
+    if constexpr (INNER) {
+      ra.load();
+      rb.load();
+    } else {
+      ra.load(k0);
+      rb.load(k0);
+    }
+  };
+  if constexpr (INNER) {
+    ra.init(A, d.am, d.ak, m0, kbeg);
+    rb.init(Bm, d.bn, d.bk, n0, kbeg);
+  } else {
+    ra.X = A; ra.sr = d.am; ra.sk = d.ak; ra.r0 = m0; ra.R = d.M; ra.K = kend; ra.vec = d.vec;
+    rb.X = Bm; rb.sr = d.bn; rb.sk = d.bk; rb.r0 = n0; rb.R = d.N; rb.K = kend; rb.vec = d.vec;
+  }
+  const int nk = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  if (nk > 0) {
+    load(kbeg);
+    ra.store(sA[0]);
+    rb.store(sB[0]);
+  }
+  for (int s = 0; s < nk; ++s) {
+    // s_waitcnt lgkmcnt(0): this wave's LDS stores of step s have landed before the
+    // barrier publishes them (written out because the barrier's own fence did not get
+    // this wait onto the loop's back edge in every build)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();
+    const bool more = s + 1 < nk;
+    if (more) load(kbeg + (s + 1) * KT);
+    const float* a_t = sA[s & 1];
+    const float* b_t = sB[s & 1];
+    f32x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = load8<float>(a_t + (wm + 16 * i + lc) * LDT + 8 * lg);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = load8<float>(b_t + (wn + 16 * j + lc) * LDT + 8 * lg);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], b[j]);
+    if (more) {
+      ra.store(sA[(s + 1) & 1]);
+      rb.store(sB[(s + 1) & 1]);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * lg + r, n = n0 + wn + 16 * j + lc;
+        if (INNER || (m < d.M && n < d.N)) C[(int64_t)m * d.ldc + n] = d.alpha * acc[i][j][r];
+      }
+}
+
 // Tiles of up to three GEMMs in one grid: blocks [0, t0) compute d0, [t0, t0 + t1) d1,
 // the rest d2. A GEMM's tiles are ordered (batch, contraction chunk, m tile, n tile).
-// Per k step: one barrier (step k in LDS, step k-1 retired), the next step's loads
-// issued into registers, this step's MFMAs, then the registers stored into the other LDS
-// buffer.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, GemmDesc d2, int t0, int t1) {
   __shared__ __attribute__((aligned(32))) float sA[2][BMG * LDT];
   __shared__ __attribute__((aligned(32))) float sB[2][BNG * LDT];
@@ -120,60 +234,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1,
   const float* const A = d.A + bi * d.a_b;
   const float* const Bm = d.B + bi * d.b_b;
   float* const C = d.C + split * d.c_split + bi * d.c_b;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
-  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
-
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  OpRegs ra, rb;
-  const int nk = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
-  if (nk > 0) {
-    ra.load(A, d.am, d.ak, d.a_kc, d.vec, m0, kbeg, d.M, kend);
-    rb.load(Bm, d.bn, d.bk, d.b_kc, d.vec, n0, kbeg, d.N, kend);
-    ra.store(sA[0], d.a_kc);
-    rb.store(sB[0], d.b_kc);
+  // wholly inside: every chunk in bounds along rows and k, so no clamps or masks
+  const bool inner = d.vec && m0 + BMG <= d.M && n0 + BNG <= d.N && kend > kbeg && (kend - kbeg) % KT == 0;
+  const int kc = d.a_kc * 2 + d.b_kc;
+  if (inner) {
+    if (kc == 3) gemm_tile<true, 1, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else if (kc == 2) gemm_tile<true, 1, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else if (kc == 1) gemm_tile<true, 0, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else gemm_tile<true, 0, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+  } else {
+    if (kc == 3) gemm_tile<false, 1, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else if (kc == 2) gemm_tile<false, 1, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else if (kc == 1) gemm_tile<false, 0, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+    else gemm_tile<false, 0, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
   }
-  for (int s = 0; s < nk; ++s) {
-    // s_waitcnt lgkmcnt(0): this wave's LDS stores of step s have landed before the
-    // barrier publishes them (written out because the barrier's own fence did not get
-    // this wait onto the loop's back edge in every build)
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __syncthreads();
-    const bool more = s + 1 < nk;
-    if (more) {
-      ra.load(A, d.am, d.ak, d.a_kc, d.vec, m0, kbeg + (s + 1) * KT, d.M, kend);
-      rb.load(Bm, d.bn, d.bk, d.b_kc, d.vec, n0, kbeg + (s + 1) * KT, d.N, kend);
-    }
-    const float* a_t = sA[s & 1];
-    const float* b_t = sB[s & 1];
-    f32x8 a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = load8<float>(a_t + (wm + 16 * i + lc) * LDT + 8 * lg);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = load8<float>(b_t + (wn + 16 * j + lc) * LDT + 8 * lg);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], b[j]);
-    if (more) {
-      ra.store(sA[(s + 1) & 1], d.a_kc);
-      rb.store(sB[(s + 1) & 1], d.b_kc);
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + 16 * i + 4 * lg + r, n = n0 + wn + 16 * j + lc;
-        if (m < d.M && n < d.N) C[(int64_t)m * d.ldc + n] = d.alpha * acc[i][j][r];
-      }
 }
 
 int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG - 1) / BNG) * d.nsplit * d.batch; }
