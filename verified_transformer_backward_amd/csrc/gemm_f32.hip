@@ -18,7 +18,13 @@
 namespace vtb {
 namespace {
 
-constexpr int BMG = 64, BNG = 64, KT = 32, LDT = KT + 8;
+constexpr int BMG = 64, BNG = 64, KT = 32, LDT = KT + 4;
+
+// LDS tiles are [row][k] with rows of LDT = 36 floats: sixteen rows read 16 bytes each at
+// one column cover all 64 banks once. Within every group of 16 rows the k index is XORed
+// with 8 * (group mod 4), which keeps each 8-float run contiguous (the operand reads take
+// 8 k) and spreads the transposing scalar stores of r-contiguous operands over the banks.
+__device__ __forceinline__ int lds_col(int r, int k) { return k ^ (((r >> 4) & 3) << 3); }
 
 struct GemmDesc {
   const float* A;
@@ -64,12 +70,13 @@ __device__ __forceinline__ void store_chunks(float* tile, const float4 (&v)[2]) 
     int r, k;
     chunk_of<KC>(threadIdx.x + 256 * e, r, k);
     if (KC) {
-      *reinterpret_cast<float4*>(tile + r * LDT + k) = v[e];
-    } else {
-      tile[(r + 0) * LDT + k] = v[e].x;
-      tile[(r + 1) * LDT + k] = v[e].y;
-      tile[(r + 2) * LDT + k] = v[e].z;
-      tile[(r + 3) * LDT + k] = v[e].w;
+      *reinterpret_cast<float4*>(tile + r * LDT + lds_col(r, k)) = v[e];
+    } else {   // rows r .. r + 3 share one 16-row group, so one column for all four
+      const int kk = lds_col(r, k);
+      tile[(r + 0) * LDT + kk] = v[e].x;
+      tile[(r + 1) * LDT + kk] = v[e].y;
+      tile[(r + 2) * LDT + kk] = v[e].z;
+      tile[(r + 3) * LDT + kk] = v[e].w;
     }
   }
 }
@@ -190,9 +197,15 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
     const float* b_t = sB[s & 1];
     f32x8 a[2], b[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = load8<float>(a_t + (wm + 16 * i + lc) * LDT + 8 * lg);
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm + 16 * i + lc;
+      a[i] = load8<float>(a_t + r * LDT + lds_col(r, 8 * lg));
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = load8<float>(b_t + (wn + 16 * j + lc) * LDT + 8 * lg);
+    for (int j = 0; j < 2; ++j) {
+      const int r = wn + 16 * j + lc;
+      b[j] = load8<float>(b_t + r * LDT + lds_col(r, 8 * lg));
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
