@@ -63,21 +63,21 @@ __device__ __forceinline__ void chunk_of(int idx, int& r, int& k) {
   k = KC ? (idx & 7) * 4 : (idx >> 4);
 }
 
+// The two chunks travel as two named float4 values rather than an array: an array member
+// that the compiler fails to keep in registers lands in scratch memory, and the wait for
+// its store then sits right behind the global loads, exposing their latency every step.
 template <int KC>
-__device__ __forceinline__ void store_chunks(float* tile, const float4 (&v)[2]) {
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    int r, k;
-    chunk_of<KC>(threadIdx.x + 256 * e, r, k);
-    if (KC) {
-      *reinterpret_cast<float4*>(tile + r * LDT + lds_col(r, k)) = v[e];
-    } else {   // rows r .. r + 3 share one 16-row group, so one column for all four
-      const int kk = lds_col(r, k);
-      tile[(r + 0) * LDT + kk] = v[e].x;
-      tile[(r + 1) * LDT + kk] = v[e].y;
-      tile[(r + 2) * LDT + kk] = v[e].z;
-      tile[(r + 3) * LDT + kk] = v[e].w;
-    }
+__device__ __forceinline__ void store_chunk(float* tile, int idx, float4 v) {
+  int r, k;
+  chunk_of<KC>(idx, r, k);
+  if (KC) {
+    *reinterpret_cast<float4*>(tile + r * LDT + lds_col(r, k)) = v;
+  } else {   // rows r .. r + 3 share one 16-row group, so one column for all four
+    const int kk = lds_col(r, k);
+    tile[(r + 0) * LDT + kk] = v.x;
+    tile[(r + 1) * LDT + kk] = v.y;
+    tile[(r + 2) * LDT + kk] = v.z;
+    tile[(r + 3) * LDT + kk] = v.w;
   }
 }
 
@@ -86,69 +86,69 @@ struct OpEdge {
   const float* X;
   int64_t sr, sk;
   int r0, R, K, vec;   // K: end of the contraction range being read
-  float4 v[2];
-  unsigned valid;      // bit 4e + i: element i of chunk e is inside the matrix
-  __device__ __forceinline__ void load(int k0) {
-    valid = 0;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      int r, k;
-      chunk_of<KC>(threadIdx.x + 256 * e, r, k);
-      const int gr = r0 + r, gk = k0 + k;
-      if (vec) {
-        const int cr = min(gr, R - (KC ? 1 : 4)), ck = min(gk, K - (KC ? 4 : 1));
-        v[e] = *reinterpret_cast<const float4*>(X + (int64_t)cr * sr + (int64_t)ck * sk);
-        if (gr < R && gk < K) valid |= 0xFu << (4 * e);
-      } else {
-        float t[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = KC ? gr : gr + i, kk = KC ? gk + i : gk;
-          t[i] = X[(int64_t)min(rr, R - 1) * sr + (int64_t)min(kk, K - 1) * sk];
-          if (rr < R && kk < K) valid |= 1u << (4 * e + i);
-        }
-        v[e] = make_float4(t[0], t[1], t[2], t[3]);
-      }
+  float4 v0, v1;
+  unsigned m0, m1;     // bit i: element i of the chunk is inside the matrix
+  __device__ __forceinline__ float4 load_chunk(int idx, int k0, unsigned& m) const {
+    int r, k;
+    chunk_of<KC>(idx, r, k);
+    const int gr = r0 + r, gk = k0 + k;
+    m = 0;
+    if (vec) {
+      const int cr = min(gr, R - (KC ? 1 : 4)), ck = min(gk, K - (KC ? 4 : 1));
+      if (gr < R && gk < K) m = 0xFu;
+      return *reinterpret_cast<const float4*>(X + (int64_t)cr * sr + (int64_t)ck * sk);
     }
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = KC ? gr : gr + i, kk = KC ? gk + i : gk;
+      t[i] = X[(int64_t)min(rr, R - 1) * sr + (int64_t)min(kk, K - 1) * sk];
+      if (rr < R && kk < K) m |= 1u << i;
+    }
+    return make_float4(t[0], t[1], t[2], t[3]);
+  }
+  __device__ __forceinline__ void load(int k0) {
+    v0 = load_chunk(threadIdx.x, k0, m0);
+    v1 = load_chunk(threadIdx.x + 256, k0, m1);
+  }
+  static __device__ __forceinline__ float4 masked(float4 v, unsigned m) {
+    return make_float4(m & 1u ? v.x : 0.f, m & 2u ? v.y : 0.f, m & 4u ? v.z : 0.f, m & 8u ? v.w : 0.f);
   }
   __device__ __forceinline__ void store(float* tile) const {
-    float4 x[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const unsigned m = valid >> (4 * e);
-      x[e] = make_float4(m & 1u ? v[e].x : 0.f, m & 2u ? v[e].y : 0.f, m & 4u ? v[e].z : 0.f, m & 8u ? v[e].w : 0.f);
-    }
-    store_chunks<KC>(tile, x);
+    store_chunk<KC>(tile, threadIdx.x, masked(v0, m0));
+    store_chunk<KC>(tile, threadIdx.x + 256, masked(v1, m1));
   }
 };
 
 template <int KC>
 struct OpInner {
-  const float* p[2];   // the thread's two chunks at the next k step
-  int64_t step;        // elements between k steps
-  float4 v[2];
+  const float *p0, *p1;   // the thread's two chunks at the next k step
+  int64_t step;           // elements between k steps
+  float4 v0, v1;
   __device__ __forceinline__ void init(const float* X, int64_t sr, int64_t sk, int r0, int k0) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      int r, k;
-      chunk_of<KC>(threadIdx.x + 256 * e, r, k);
-      p[e] = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
-    }
+    int r, k;
+    chunk_of<KC>(threadIdx.x, r, k);
+    p0 = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
+    chunk_of<KC>(threadIdx.x + 256, r, k);
+    p1 = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
     step = (int64_t)KT * sk;
   }
   __device__ __forceinline__ void load() {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      v[e] = *reinterpret_cast<const float4*>(p[e]);
-      p[e] += step;
-    }
+    v0 = *reinterpret_cast<const float4*>(p0);
+    v1 = *reinterpret_cast<const float4*>(p1);
+    p0 += step;
+    p1 += step;
   }
-  __device__ __forceinline__ void store(float* tile) const { store_chunks<KC>(tile, v); }
+  __device__ __forceinline__ void store(float* tile) const {
+    store_chunk<KC>(tile, threadIdx.x, v0);
+    store_chunk<KC>(tile, threadIdx.x + 256, v1);
+  }
 };
 
 // One 64 x 64 tile of C = alpha A B over k in [kbeg, kend). Per k step: one barrier (step k
 // in LDS, step k-1 retired), the next step's loads issued into registers, this step's
-// MFMAs, then the registers stored into the other LDS buffer.
+// MFMAs, then the registers stored into the other LDS buffer. The last step, which loads
+// nothing, is peeled off so that the loop body holds no branch around its loads.
 template <bool INNER, int AKC, int BKC>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, const float* Bm, float* C, int m0, int n0,
                                           int kbeg, int kend, float (*sA)[BMG * LDT], float (*sB)[BNG * LDT]) {
@@ -185,16 +185,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
     ra.store(sA[0]);
     rb.store(sB[0]);
   }
-  for (int s = 0; s < nk; ++s) {
-    // s_waitcnt lgkmcnt(0): this wave's LDS stores of step s have landed before the
-    // barrier publishes them (written out because the barrier's own fence did not get
-    // this wait onto the loop's back edge in every build)
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __syncthreads();
-    const bool more = s + 1 < nk;
-    if (more) load(kbeg + (s + 1) * KT);
-    const float* a_t = sA[s & 1];
-    const float* b_t = sB[s & 1];
+  auto step_mma = [&](int buf) {
+    const float* a_t = sA[buf];
+    const float* b_t = sB[buf];
     f32x8 a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -210,10 +203,27 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], b[j]);
-    if (more) {
-      ra.store(sA[(s + 1) & 1]);
-      rb.store(sB[(s + 1) & 1]);
-    }
+  };
+  // s_waitcnt lgkmcnt(0) before each barrier: this wave's LDS stores of the step have
+  // landed before the barrier publishes them (written out because the barrier's own fence
+  // did not get this wait onto the loop's back edge in every build)
+  for (int s = 0; s + 1 < nk; ++s) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();
+    load(kbeg + (s + 1) * KT);
+    // keep the loads ahead of the MFMAs and the LDS stores (which wait for the loads)
+    // behind them: left alone, the scheduler moves one or the other across the MFMAs and
+    // the load latency shows
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(s & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ra.store(sA[(s + 1) & 1]);
+    rb.store(sB[(s + 1) & 1]);
+  }
+  if (nk > 0) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();
+    step_mma((nk - 1) & 1);
   }
 
 #pragma unroll
