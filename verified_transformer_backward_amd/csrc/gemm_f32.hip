@@ -123,15 +123,15 @@ struct OpEdge {
 template <int KC>
 struct OpInner {
   const float *p0, *p1;   // the thread's two chunks at the next k step
-  int64_t step;           // elements between k steps
+  int64_t step;           // elements between consecutive loads (nstep k steps)
   float4 v0, v1;
-  __device__ __forceinline__ void init(const float* X, int64_t sr, int64_t sk, int r0, int k0) {
+  __device__ __forceinline__ void init(const float* X, int64_t sr, int64_t sk, int r0, int k0, int nstep) {
     int r, k;
     chunk_of<KC>(threadIdx.x, r, k);
     p0 = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
     chunk_of<KC>(threadIdx.x + 256, r, k);
     p1 = X + (int64_t)(r0 + r) * sr + (int64_t)(k0 + k) * sk;
-    step = (int64_t)KT * sk;
+    step = (int64_t)nstep * KT * sk;
   }
   __device__ __forceinline__ void load() {
     v0 = *reinterpret_cast<const float4*>(p0);
@@ -161,10 +161,27 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  typename std::conditional<INNER, OpInner<AKC>, OpEdge<AKC>>::type ra;
-  typename std::conditional<INNER, OpInner<BKC>, OpEdge<BKC>>::type rb;
-  auto load = [&](int k0) {
+  // Two register sets per operand: set 0 carries the even k steps, set 1 the odd ones, so
+  // a step's loads are issued two steps before its LDS store and have a whole step of
+  // MFMAs more to land.
+  using OpA = typename std::conditional<INNER, OpInner<AKC>, OpEdge<AKC>>::type;
+  using OpB = typename std::conditional<INNER, OpInner<BKC>, OpEdge<BKC>>::type;
+  OpA ra0, ra1;
+  OpB rb0, rb1;
+  if constexpr (INNER) {
+    ra0.init(A, d.am, d.ak, m0, kbeg, 2);
+    rb0.init(Bm, d.bn, d.bk, n0, kbeg, 2);
+    ra1.init(A, d.am, d.ak, m0, kbeg + KT, 2);
+    rb1.init(Bm, d.bn, d.bk, n0, kbeg + KT, 2);
+  } else {
+    ra0.X = A; ra0.sr = d.am; ra0.sk = d.ak; ra0.r0 = m0; ra0.R = d.M; ra0.K = kend; ra0.vec = d.vec;
+    rb0.X = Bm; rb0.sr = d.bn; rb0.sk = d.bk; rb0.r0 = n0; rb0.R = d.N; rb0.K = kend; rb0.vec = d.vec;
+    ra1 = ra0;
+    rb1 = rb0;
+  }
+  auto load = [&](auto& ra, auto& rb, int k0) {
     if constexpr (INNER) {
+      (void)k0;
       ra.load();
       rb.load();
     } else {
@@ -172,19 +189,6 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
       rb.load(k0);
     }
   };
-  if constexpr (INNER) {
-    ra.init(A, d.am, d.ak, m0, kbeg);
-    rb.init(Bm, d.bn, d.bk, n0, kbeg);
-  } else {
-    ra.X = A; ra.sr = d.am; ra.sk = d.ak; ra.r0 = m0; ra.R = d.M; ra.K = kend; ra.vec = d.vec;
-    rb.X = Bm; rb.sr = d.bn; rb.sk = d.bk; rb.r0 = n0; rb.R = d.N; rb.K = kend; rb.vec = d.vec;
-  }
-  const int nk = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
-  if (nk > 0) {
-    load(kbeg);
-    ra.store(sA[0]);
-    rb.store(sB[0]);
-  }
   auto step_mma = [&](int buf) {
     const float* a_t = sA[buf];
     const float* b_t = sB[buf];
@@ -204,27 +208,54 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
 #pragma unroll
       for (int j = 0; j < 2; ++j) mma(acc[i][j], a[i], b[j]);
   };
-  // s_waitcnt lgkmcnt(0) before each barrier: this wave's LDS stores of the step have
-  // landed before the barrier publishes them (written out because the barrier's own fence
-  // did not get this wait onto the loop's back edge in every build)
-  for (int s = 0; s + 1 < nk; ++s) {
+  // Step s: LDS buffer s & 1 holds step s. Set L = s & 1 was stored at step s - 1 and now
+  // takes step s + 2; the other set, loaded at step s - 1, holds step s + 1 and is stored
+  // into the other buffer after the MFMAs.
+  //   s_waitcnt lgkmcnt(0) before each barrier: this wave's LDS stores have landed before
+  //   the barrier publishes them (written out because the barrier's own fence did not get
+  //   this wait onto the loop's back edge in every build).
+  //   The scheduling barriers keep the loads ahead of the MFMAs and the LDS stores (which
+  //   wait for loads) behind them: left alone, the scheduler moves one or the other across
+  //   the MFMAs and the load latency shows.
+  auto body = [&](auto set, int s, bool ld, bool st) {
+    constexpr int L = decltype(set)::value;
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __syncthreads();
-    load(kbeg + (s + 1) * KT);
-    // keep the loads ahead of the MFMAs and the LDS stores (which wait for the loads)
-    // behind them: left alone, the scheduler moves one or the other across the MFMAs and
-    // the load latency shows
+    if (ld) {
+      if constexpr (L == 0) load(ra0, rb0, kbeg + (s + 2) * KT);
+      else load(ra1, rb1, kbeg + (s + 2) * KT);
+    }
     __builtin_amdgcn_sched_barrier(0);
     step_mma(s & 1);
     __builtin_amdgcn_sched_barrier(0);
-    ra.store(sA[(s + 1) & 1]);
-    rb.store(sB[(s + 1) & 1]);
-  }
+    if (st) {
+      if constexpr (L == 0) {
+        ra1.store(sA[(s + 1) & 1]);
+        rb1.store(sB[(s + 1) & 1]);
+      } else {
+        ra0.store(sA[(s + 1) & 1]);
+        rb0.store(sB[(s + 1) & 1]);
+      }
+    }
+  };
+  const std::integral_constant<int, 0> set0;
+  const std::integral_constant<int, 1> set1;
+  const int nk = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
   if (nk > 0) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __syncthreads();
-    step_mma((nk - 1) & 1);
+    load(ra0, rb0, kbeg);
+    if (nk > 1) load(ra1, rb1, kbeg + KT);
+    ra0.store(sA[0]);
+    rb0.store(sB[0]);
   }
+  int s = 0;
+  for (; s + 3 < nk; s += 2) {
+    body(set0, s, true, true);
+    body(set1, s + 1, true, true);
+  }
+  // the last one to three steps (s is even here)
+  if (s < nk) body(set0, s, s + 2 < nk, s + 1 < nk);
+  if (s + 1 < nk) body(set1, s + 1, false, s + 2 < nk);
+  if (s + 2 < nk) body(set0, s + 2, false, false);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
