@@ -270,7 +270,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, const float* A, con
 
 // Tiles of up to three GEMMs in one grid: blocks [0, t0) compute d0, [t0, t0 + t1) d1,
 // the rest d2. A GEMM's tiles are ordered (batch, contraction chunk, m tile, n tile).
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, GemmDesc d2, int t0, int t1) {
+__global__ __launch_bounds__(256, 4) void gemm_f32_kernel(GemmDesc d0, GemmDesc d1, GemmDesc d2, int t0, int t1) {
   __shared__ __attribute__((aligned(32))) float sA[2][BMG * LDT];
   __shared__ __attribute__((aligned(32))) float sB[2][BNG * LDT];
   const int bid = blockIdx.x;
