@@ -88,7 +88,10 @@ def test_fused_rope_rmsnorm_residual(T, H, d, layout, pos0, inplace):
     assert_close("fused", host(out), ref, TOL["f32"])
 
 
-@pytest.mark.parametrize("T,K,N", [(100, 72, 50), (64, 64, 64), (256, 2560, 2560), (3, 130, 7)])
+# k-step counts (32 deep) of dX / dW: (2, 4), (2, 2), (80, 8), (1, 1), (5, 3), (3, 5): the
+# GEMM's two-set pipeline ends on one, two or three steps depending on that count
+@pytest.mark.parametrize("T,K,N", [(100, 72, 50), (64, 64, 64), (256, 2560, 2560), (3, 130, 7), (96, 80, 150),
+                                   (160, 40, 70)])
 def test_linear_shapes(T, K, N):
     need_gpu()
     say(f"linear T {T} K {K} N {N}")
