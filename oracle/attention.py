@@ -85,6 +85,44 @@ def attention_forward(q, k, v, scale: float, causal: bool, want_p: bool = False,
     return O, lse
 
 
+def attention_forward_online(q, k, v, scale: float, causal: bool):
+    """The same forward by the online softmax that the Hesper pull request's commit log
+    describes for FlashAttention.lean (flashAttentionSpec: K and V consumed one position
+    at a time, stated equal to the standard scores -> softmax -> apply form).
+
+    Per query row: a running maximum m, a running sum of exponentials l and a running
+    weighted sum u of value rows. Each visible key j with score s rescales l and u by
+    exp(m_old - m_new) before adding exp(s - m_new) and exp(s - m_new) v_j; at the end
+    O = u / l and lse = m + ln l. Plain loops over rows and keys: small cases only.
+
+    Returns (O [B,Tq,Hq,d], lse [B,Hq,Tq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    g = _group(Hq, Hkv)
+    O = np.zeros((B, Tq, Hq, d))
+    lse = np.zeros((B, Hq, Tq))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            for i in range(Tq):
+                m, l, u = -np.inf, 0.0, np.zeros(d)
+                for j in range(Tk):
+                    if causal and j > i + (Tk - Tq):
+                        break
+                    s = scale * float(q[b, i, h] @ k[b, j, kv])
+                    m_new = max(m, s)
+                    a = np.exp(m - m_new)     # 0 for the first key (m = -inf)
+                    e = np.exp(s - m_new)
+                    l = l * a + e
+                    u = u * a + e * v[b, j, kv]
+                    m = m_new
+                O[b, i, h] = u / l
+                lse[b, h, i] = m + np.log(l)
+    return O, lse
+
+
 def attention_lse(q, k, scale: float, causal: bool, row_block: int = 1024, q_heads=None):
     """Row log-sum-exp of the scaled scores over visible keys, [B, Hq, Tq].
 

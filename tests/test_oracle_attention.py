@@ -193,3 +193,50 @@ def test_bottom_right_causal_alignment():
     vis = A.visible_keys(3, 7, True)
     assert vis[2].all() and vis[0].sum() == 5
     assert np.array_equal(A.visible_keys(4, 4, True), np.tril(np.ones((4, 4), bool)))
+
+
+# ---- forward by online softmax (the FlashAttention.lean entry of the commit log)
+
+@pytest.mark.parametrize("causal,Hq,Hkv,Tq,Tk", [(True, 2, 2, 7, 7), (True, 4, 2, 3, 9), (False, 2, 1, 5, 6)])
+def test_online_forward_equals_standard(causal, Hq, Hkv, Tq, Tk):
+    # flash == standard, the equivalence the commit log states; the standard form is
+    # pinned by the hand fixtures, central differences and autograd above
+    x = synth.attention_inputs(2, Tq, Tk, Hq, Hkv, 8, seed=31 + Tq)
+    O1, l1 = A.attention_forward(x["q"], x["k"], x["v"], 0.4, causal)
+    O2, l2 = A.attention_forward_online(x["q"], x["k"], x["v"], 0.4, causal)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("fwd", [A.attention_forward, A.attention_forward_online])
+def test_forward_zero_keys_average_visible_values(fwd):
+    # all scores 0: P uniform over the visible keys, O_i = mean of visible v_j, lse = ln(count)
+    x = synth.attention_inputs(1, 5, 8, 2, 2, 4, seed=32)
+    k = np.zeros_like(x["k"])
+    O, lse = fwd(x["q"], k, x["v"], 0.9, True)
+    v = x["v"].astype(np.float64)
+    for i in range(5):
+        n = i + 3 + 1   # keys 0 .. i + (8 - 5)
+        np.testing.assert_allclose(O[0, i], v[0, :n].mean(axis=0), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=1e-14)
+
+
+@pytest.mark.parametrize("fwd", [A.attention_forward, A.attention_forward_online])
+def test_forward_single_key_copies_value(fwd):
+    # Tk = 1: P = 1, O = v_0, lse = the one scaled score
+    x = synth.attention_inputs(1, 1, 1, 3, 1, 8, seed=33)
+    O, lse = fwd(x["q"], x["k"], x["v"], 0.3, True)
+    q, k, v = (x[n].astype(np.float64) for n in ("q", "k", "v"))
+    np.testing.assert_allclose(O[0, 0], np.repeat(v[0, 0], 3, axis=0), rtol=0, atol=0)
+    np.testing.assert_allclose(lse[0, :, 0], 0.3 * q[0, 0] @ k[0, 0, 0], rtol=1e-15)
+
+
+def test_online_forward_large_scores_stay_finite():
+    # scores far beyond exp's range: the running maximum keeps every term finite
+    x = synth.attention_inputs(1, 4, 4, 1, 1, 8, seed=34)
+    q = x["q"].astype(np.float64) * 400.0
+    O1, l1 = A.attention_forward(q, x["k"], x["v"], 1.0, True)
+    O2, l2 = A.attention_forward_online(q, x["k"], x["v"], 1.0, True)
+    assert np.all(np.isfinite(O2)) and np.all(np.isfinite(l2))
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12)
