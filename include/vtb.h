@@ -110,6 +110,22 @@ int attn_bwd_timed(const attn_bwd_desc* desc, const void* q, const void* k, cons
 int attn_fwd_lse(const attn_bwd_desc* desc, const void* q, const void* k, float* lse,
                  vtb_stream_t stream);
 
+/* Attention forward by online softmax: the FlashAttention.lean entry of the Hesper pull
+ * request's commit log (flashAttentionSpec: K and V consumed one position at a time with a
+ * running maximum and sum of exponentials, equal to scores -> softmax -> apply), over the
+ * softmax and apply of "Attention (full single-head)" (attentionForward), batched with
+ * the same heads, grouping and causal mask as attn_bwd:
+ *     O_i = sum_j P_ij v_j,  P_ij = exp(scale q_i . k_j - lse_i) over visible j,
+ *     lse_i = ln sum_{visible j} exp(scale q_i . k_j).
+ * q: [B, Tq, Hq, D], k, v: [B, Tk, Hkv, D] in desc->in_dtype with strides s_q, s_k, s_v.
+ * o (written): [B, Tq, Hq, D] in desc->out_dtype with strides s_dq (o has dq's shape).
+ * lse (written, may be NULL): [B, Hq, Tq] fp32, the input attn_bwd takes.
+ * All pointers device memory owned by the caller, 16-byte aligned; o and lse must not
+ * overlap the inputs or each other (VTB_ERR_ALIAS). One kernel on `stream`; nothing is
+ * written on an error. bf16 inputs use bf16 P in the P V product, fp32 accumulation. */
+int attn_fwd(const attn_bwd_desc* desc, const void* q, const void* k, const void* v, void* o,
+             float* lse, vtb_stream_t stream);
+
 /* ---------------------------------------------------------------------------------------
  * RoPE backward: "Hesper.Training.VerifiedBackward", section "RoPE (Rotary Position
  * Embedding)", ropeBackward = rotation by -theta:

@@ -5,7 +5,7 @@ provides device memory (tensors) and the current HIP stream. There is no fallbac
 libvtb.so is missing or a call fails, an exception is raised.
 
 Entry points (same names as the C ABI in include/vtb.h):
-    attn_bwd, attn_fwd_lse, rope_bwd, rmsnorm_bwd, rope_rmsnorm_res_bwd, linear_bwd,
+    attn_bwd, attn_fwd, attn_fwd_lse, rope_bwd, rmsnorm_bwd, rope_rmsnorm_res_bwd, linear_bwd,
     layer_bwd, plus the workspace-size queries.
 Attention tensors use the [B, T, H, D] layout (any strides, D contiguous).
 """
@@ -26,7 +26,7 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
-    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd_lse",
+    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd",
     "layer_bwd_workspace_size", "layer_bwd",
 )
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "attn_bwd_timed": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P,
                                           ctypes.POINTER(ctypes.c_void_p), I32]),
         "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
+        "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P]),
         "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
         "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
         "rope_rmsnorm_res_bwd": (ctypes.c_int, [P, F32, P, P, P, P, I32, I32, I32, I32, F64, I32, F32, P]),
@@ -180,6 +181,24 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dt
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib().attn_bwd_timed(*args, arr, len(events)), "attn_bwd_timed")
     return dq, dk, dv
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool, out_dtype=None, o=None, lse=None, want_lse: bool = True,
+             stream=None):
+    """Attention forward (see include/vtb.h): returns (o [B, Tq, Hq, D], lse [B, Hq, Tq] fp32
+    or None when want_lse is false and no lse tensor is given)."""
+    for t, n in ((k, "k"), (v, "v")):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise TypeError(f"{n} must match q's dtype and device")
+    out_dtype = out_dtype or q.dtype
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device) if o is None else o
+    B, Tq, Hq, _ = q.shape
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    desc = make_attn_desc(q, k, scale, causal, out_dtype=o.dtype, dq=o, v=v)
+    _check(lib().attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
+           "attn_fwd")
+    return o, lse
 
 
 def attn_fwd_lse(q, k, scale: float, causal: bool, lse=None, stream=None):

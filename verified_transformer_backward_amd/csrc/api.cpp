@@ -291,6 +291,44 @@ int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* ls
   return hip_status(vtb::launch_flash_dq(p, vtb::ROW_LSE_ONLY, reinterpret_cast<hipStream_t>(stream)), "lse pass");
 }
 
+int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
+             vtb_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_desc(d, false);
+  if (rc) return rc;
+  if (!valid_dtype(d->out_dtype)) return fail(VTB_ERR_ARG, "out_dtype=%d", d->out_dtype);
+  const int64_t* st[2] = {d->s_v, d->s_dq};
+  const char* names[2] = {"v", "o (s_dq)"};
+  for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (st[t][i] < 0) return fail(VTB_ERR_ARG, "%s stride %d is negative", names[t], i);
+      if (st[t][i] % 8) return fail(VTB_ERR_UNSUPPORTED, "%s stride %d = %lld is not a multiple of 8 elements", names[t], i, (long long)st[t][i]);
+    }
+  const size_t ein = esize(d->in_dtype), eout = esize(d->out_dtype);
+  const size_t rows = (size_t)d->B * d->Hq * d->Tq;
+  if (rows == 0) return VTB_OK;
+  if (!q || !k || !v || !o) return fail(VTB_ERR_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(VTB_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+  const Span so = span_of(o, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_dq, eout));
+  const Span sq = span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein));
+  const Span sk = span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein));
+  const Span sv = span_of(v, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_v, ein));
+  if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv)) return fail(VTB_ERR_ALIAS, "o overlaps q, k or v");
+  if (lse) {
+    const Span sl = span_of(lse, rows * 4);
+    if (overlap(sl, sq) || overlap(sl, sk) || overlap(sl, sv) || overlap(sl, so))
+      return fail(VTB_ERR_ALIAS, "lse overlaps q, k, v or o");
+  }
+  vtb::AttnParams p = make_params(d);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dq = o;
+  p.lse_out = lse;
+  return hip_status(vtb::launch_flash_dq(p, vtb::ROW_FWD, reinterpret_cast<hipStream_t>(stream)), "forward pass");
+}
+
 int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,
              const int32_t* pos, int32_t pos0, double base, int32_t layout, vtb_stream_t stream) {
   g_last_error.clear();

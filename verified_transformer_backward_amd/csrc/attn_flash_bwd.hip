@@ -91,7 +91,8 @@ void flash_dq_kernel(AttnParams p) {
   constexpr int BN = 64;                   // keys per staged block
   constexpr int NKS = D / 32, NDT = D / 16;
   constexpr bool kNeedS = MODE != ROW_P_GIVEN;
-  constexpr bool kNeedDP = MODE != ROW_LSE_ONLY;
+  constexpr bool kNeedDP = MODE != ROW_LSE_ONLY && MODE != ROW_FWD;
+  constexpr bool kNeedV = kNeedDP || MODE == ROW_FWD;   // V staged: dP operand, or P V in the forward
   constexpr bool kOnline = MODE == ROW_LSE_COMPUTE || MODE == ROW_LSE_ONLY;
   __shared__ __attribute__((aligned(32))) char smem[dq_smem_bytes<E, D>()];
   E* sK = reinterpret_cast<E*>(smem);
@@ -148,19 +149,106 @@ void flash_dq_kernel(AttnParams p) {
   auto stage_block = [&](int jb) {
     __syncthreads();
     kt_regs.template store<L>(sK);   // K: S^T operand and, in sweep 2, the dQ operand
-    if constexpr (kNeedDP) vt_regs.template store<L>(sV);
+    if constexpr (kNeedV) vt_regs.template store<L>(sV);
     __syncthreads();
     if (jb + BN < kend) {
       kt_regs.load(p.k, p.sk, b, kvh, jb + BN, Tk);
-      if constexpr (kNeedDP) vt_regs.load(p.v, p.sv, b, kvh, jb + BN, Tk);
+      if constexpr (kNeedV) vt_regs.load(p.v, p.sv, b, kvh, jb + BN, Tk);
     }
   };
   auto start_sweep = [&]() {
     if (kend > 0) {
       kt_regs.load(p.k, p.sk, b, kvh, 0, Tk);
-      if constexpr (kNeedDP) vt_regs.load(p.v, p.sv, b, kvh, 0, Tk);
+      if constexpr (kNeedV) vt_regs.load(p.v, p.sv, b, kvh, 0, Tk);
     }
   };
+  // acc^T (lane: d = 16 dt + 4 lg + r of the lane's query) times mult, transposed to
+  // query-major rows through LDS, then stored as rows of dq (dQ, or O in the forward).
+  auto store_rows = [&](const f32x4 (&accT)[NDT], float mult) {
+    __syncthreads();
+    float* stage = reinterpret_cast<float*>(smem) + w * 16 * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stage[lc * (D + 4) + 16 * dt + 4 * lg + r] = accT[dt][r] * mult;
+    __syncthreads();
+    const int rl = lane >> 2;
+    const int qo = qb * BM + 16 * w + rl;
+    if (qo < Tq) {
+      const int64_t o = (int64_t)b * p.sdq[0] + (int64_t)qo * p.sdq[1] + (int64_t)h * p.sdq[2];
+      const float* src = stage + rl * (D + 4);
+      constexpr int PER = D / 4;
+      const int c0 = (lane & 3) * PER;
+      if (p.out_bf16) {
+        __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + o;
+#pragma unroll
+        for (int c = 0; c < PER; c += 8) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[c0 + c + e];
+          *reinterpret_cast<bf16x8*>(dst + c0 + c) = v;
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(p.dq) + o;
+#pragma unroll
+        for (int c = 0; c < PER; c += 4)
+          *reinterpret_cast<float4*>(dst + c0 + c) = make_float4(src[c0 + c], src[c0 + c + 1], src[c0 + c + 2], src[c0 + c + 3]);
+      }
+    }
+  };
+
+  if constexpr (MODE == ROW_FWD) {
+    // ---- forward, one sweep with online softmax. Every 16-lane group holds other keys
+    // of the lane's query, so each block's maximum is taken over the four groups first:
+    // then all of a query's probabilities share one reference and feed one MFMA.
+    f32x4 oT[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;   // log2-domain running maximum; this lane's sum of exponentials
+    start_sweep();
+    for (int jb = 0; jb < kend; jb += BN) {
+      stage_block(jb);
+      f32x4 sT[4], dpT[4];
+      block_scores(sT, dpT);
+      float s2[4][4], bm = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb + 16 * kt + 4 * lg + r;
+          const bool vis = qok & (j < Tk) & (!p.causal | (j <= qrow + off));
+          s2[kt][r] = vis ? sT[kt][r] * sl2 : -INFINITY;
+          bm = fmaxf(bm, s2[kt][r]);
+        }
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m, bm);
+      const float mref = mn == -INFINITY ? 0.f : mn;    // no visible key yet: every term is 0
+      const float a = __builtin_amdgcn_exp2f(m - mref);  // 0 while m is -inf
+      l *= a;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oT[dt] *= a;
+      frag_t<E> pb[2];   // keys 32c + 4lg + (0..3) and 32c + 16 + 4lg + (0..3)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s2[kt][r] - mref);
+          l += e;
+          pb[kt >> 1][4 * (kt & 1) + r] = from_f32<E>(e);
+        }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) mma(oT[dt], col8<L>(sV, 32 * c + 4 * lg, 32 * c + 16 + 4 * lg, 16 * dt), pb[c]);
+      m = mn;
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (lg == 0 && qok && p.lse_out) p.lse_out[rowbase + qrow] = (m + log2f(l)) * kLn2;
+    store_rows(oT, l > 0.f ? 1.f / l : 0.f);
+    return;
+  }
   auto prob = [&](float s_t, int j) -> float {   // P of (this lane's query, key j), 0 when invisible
     const bool vis = qok & (j < Tk) & (!p.causal | (j <= qrow + off));
     if constexpr (MODE == ROW_P_GIVEN) {
@@ -245,37 +333,8 @@ void flash_dq_kernel(AttnParams p) {
         for (int c = 0; c < 2; ++c) mma(dqT[dt], col8<L>(sK, 32 * c + 4 * lg, 32 * c + 16 + 4 * lg, 16 * dt), dsb[c]);
     }
 
-    // dQ = scale dQ^T, transposed to query-major rows through LDS, then row stores.
-    __syncthreads();
-    float* stage = reinterpret_cast<float*>(smem) + w * 16 * (D + 4);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) stage[lc * (D + 4) + 16 * dt + 4 * lg + r] = dqT[dt][r] * p.scale;
-    __syncthreads();
-    const int rl = lane >> 2;
-    const int qo = qb * BM + 16 * w + rl;
-    if (qo < Tq) {
-      const int64_t o = (int64_t)b * p.sdq[0] + (int64_t)qo * p.sdq[1] + (int64_t)h * p.sdq[2];
-      const float* src = stage + rl * (D + 4);
-      constexpr int PER = D / 4;
-      const int c0 = (lane & 3) * PER;
-      if (p.out_bf16) {
-        __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + o;
-#pragma unroll
-        for (int c = 0; c < PER; c += 8) {
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)src[c0 + c + e];
-          *reinterpret_cast<bf16x8*>(dst + c0 + c) = v;
-        }
-      } else {
-        float* dst = reinterpret_cast<float*>(p.dq) + o;
-#pragma unroll
-        for (int c = 0; c < PER; c += 4)
-          *reinterpret_cast<float4*>(dst + c0 + c) = make_float4(src[c0 + c], src[c0 + c + 1], src[c0 + c + 2], src[c0 + c + 3]);
-      }
-    }
+    // dQ = scale dQ^T
+    store_rows(dqT, p.scale);
   }
 }
 
@@ -479,6 +538,7 @@ hipError_t dq_dispatch(const AttnParams& p, int mode, hipStream_t s, KernelEvent
     case ROW_LSE_GIVEN: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
     case ROW_LSE_COMPUTE: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_COMPUTE>, grid, dim3(kThreads), 0, s, ev, p); break;
     case ROW_LSE_ONLY: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_ONLY>, grid, dim3(kThreads), 0, s, ev, p); break;
+    case ROW_FWD: launch_kernel(flash_dq_kernel<E, D, ROW_FWD>, grid, dim3(kThreads), 0, s, ev, p); break;
     default: launch_kernel(flash_dq_kernel<E, D, ROW_P_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
   }
   return hipGetLastError();

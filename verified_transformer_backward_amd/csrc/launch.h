@@ -45,8 +45,10 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 }
 
 // How the query-parallel pass obtains P: from the given lse, by computing lse itself
-// (online max/sum), lse only (no backward), or from a saved softmax P.
-enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3 };
+// (online max/sum), lse only (no backward), or from a saved softmax P. ROW_FWD is the
+// forward: O = softmax(scale Q K^T) V by online softmax, written through dq / sdq, and
+// lse written to lse_out when that is not null.
+enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3, ROW_FWD = 4 };
 
 // Flash-style path (any Tq): query-parallel pass (row term D, lse when computed, dQ),
 // then key-parallel pass (dK, dV). The second reads D (and lse) written by the first.
