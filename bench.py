@@ -152,7 +152,7 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain")
+EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd")
 
 
 def extra_workloads(torch, vtb, hip, only=None):
@@ -209,6 +209,23 @@ def extra_workloads(torch, vtb, hip, only=None):
                               "roofline": {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                                            "algorithmic_flops": fl}}
         del t, o, ws, lse
+
+    if want("attn_fwd"):
+        # attention forward (O and lse, online softmax) on the training shape: causal B4 H20 T512 d128 bf16
+        x = synth.causal_inputs()
+        t = {n: up(x[n], "bf16") for n in ("q", "k", "v")}
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((4, 20, 512), dtype=torch.float32, device=dev)
+        f = lambda: vtb.attn_fwd(t["q"], t["k"], t["v"], x["scale"], True, o=o, lse=lse, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        fl = 4 * 128 * 4 * 20 * 512 * 513 // 2     # S and P V: 2 contractions of 2 d FLOP per visible pair
+        byts = 4 * t["q"].numel() * 2 + lse.numel() * 4   # q, k, v read, o written (bf16), lse written
+        out["attn_fwd"] = {"workload": "attention forward (O, lse), causal B4 H20 T512 d128 bf16", "ms": round(ms, 5),
+                           "value": round(fl / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                           "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
+                           "roofline": {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                        "algorithmic_flops": fl, "algorithmic_bytes": byts}}
+        del t, o, lse
 
     if want("rope_rmsnorm_res") or want("rope_bwd") or want("rmsnorm_bwd"):
         # fused RoPE -> RMSNorm -> residual tail on the stack shape (30 x 256 rows, hidden 2560), fp32

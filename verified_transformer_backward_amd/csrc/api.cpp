@@ -326,7 +326,9 @@ int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
   p.v = v;
   p.dq = o;
   p.lse_out = lse;
-  return hip_status(vtb::launch_flash_dq(p, vtb::ROW_FWD, reinterpret_cast<hipStream_t>(stream)), "forward pass");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (vtb::mfma_fwd_applicable(p)) return hip_status(vtb::launch_mfma_fwd(p, s), "forward pass (MFMA)");
+  return hip_status(vtb::launch_flash_dq(p, vtb::ROW_FWD, s), "forward pass");
 }
 
 int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,

@@ -367,6 +367,213 @@ void dq_mfma_kernel(AttnParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------ forward
+// Online-softmax forward on the dq pass's layout: per 64-key block the wave computes
+// S^T = K Q^T (a lane owns one query column), takes the block's maximum over its four
+// 16-lane groups, rescales its running sums and O^T by exp(m_old - m_new), then
+// O^T += V^T P^T with V^T from LDS transpose reads. O is normalised by the sum of the
+// bf16-rounded P that entered the MFMAs, so a query's weights sum to one as applied; lse
+// comes from the fp32 sum.
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
+void fwd_mfma_kernel(AttnParams p) {
+  constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BN * kHD];   // [buffer][K, V]
+
+  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const int nqb = (p.Tq + BM - 1) / BM;
+  const int qb = nqb - 1 - (int)blockIdx.y;   // causal: heaviest query block first
+  const int G = p.Hq / p.Hkv, kvh = h / G;
+  const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
+  const float sl2 = p.scale * kLog2e;
+  const int64_t rowbase = ((int64_t)b * p.Hq + h) * Tq;
+  const int qw0 = qb * BM + QW * w;
+
+  const __bf16* Qh = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.sq[0] + (int64_t)h * p.sq[2];
+  const __bf16* Kh = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.sk[0] + (int64_t)kvh * p.sk[2];
+  const __bf16* Vh = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.sv[0] + (int64_t)kvh * p.sv[2];
+
+  bf16x8 qa[kNT][kNKS];   // Q of the lane's queries: B operand (k = d, n = query) of S^T
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    const int i = min(qw0 + 16 * qt + lc, Tq - 1);
+#pragma unroll
+    for (int ks = 0; ks < kNKS; ++ks) qa[qt][ks] = load8<__bf16>(Qh + (int64_t)i * p.sq[1] + 32 * ks + 8 * lg);
+  }
+  f32x4 acO[kNDT][kNT];
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < kNT; ++qt) acO[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // log2-domain running maximum (shared by the query's four lane groups), and this lane's
+  // running sums of exp (fp32) and of the bf16-rounded exp
+  float mrun[kNT], lrun[kNT], lrnd[kNT];
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    mrun[qt] = -INFINITY;
+    lrun[qt] = lrnd[qt] = 0.f;
+  }
+
+  const int last_row = min(Tq, (qb + 1) * BM) - 1;
+  const int kend = p.causal ? min(Tk, last_row + off + 1) : Tk;
+  const int nblk = (kend + BN - 1) / BN;
+  const int wkend = qw0 >= Tq ? 0 : (p.causal ? min(Tk, min(Tq - 1, qw0 + QW - 1) + off + 1) : Tk);
+
+  RowStager kst, vst;
+  kst.init(w, p.sk[1]);
+  vst.init(w, p.sv[1]);
+  wait_loads();
+  const uint32_t sm_lds = lds_addr(&sm[0][0][0]);
+  constexpr uint32_t kTileBytes = 2u * BN * kHD;
+  if (nblk > 0) {
+    kst.stage(sm_lds, Kh, p.sk[1], 0, Tk);
+    vst.stage(sm_lds + kTileBytes, Vh, p.sv[1], 0, Tk);
+  }
+
+  auto block = [&](auto buf_c, int jb, bool full, auto&& dma) {
+    const __bf16* sK = sm[decltype(buf_c)::value][0];
+    const __bf16* sV = sm[decltype(buf_c)::value][1];
+    f32x4 sT[4][kNT];
+    bf16x8 fk[2][kNKS];
+    auto read_rows = [&](int kt, bf16x8(&ak)[kNKS]) {
+#pragma unroll
+      for (int ks = 0; ks < kNKS; ++ks) ak[ks] = row8<LT>(sK, 16 * kt + lc, 32 * ks + 8 * lg);
+    };
+    read_rows(0, fk[0]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (kt + 1 < 4) read_rows(kt + 1, fk[(kt + 1) & 1]);
+      if (kt == 0 || kt == 2) dma(kt >> 1);
+      fence();
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt) {
+        sT[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kNKS; ++ks) mma(sT[kt][qt], fk[kt & 1][ks], qa[qt][ks]);
+      }
+      fence();
+    }
+    // V^T fragments of the first (dt, c) pairs are read under the softmax arithmetic.
+    constexpr int NP = kNDT * 2, AHEAD = 4;
+    bf16x8 vT[AHEAD + 1];
+    auto read_vT = [&](int pr) { return col8<LT>(sV, 32 * (pr & 1) + 4 * lg, 32 * (pr & 1) + 16 + 4 * lg, 16 * (pr >> 1)); };
+#pragma unroll
+    for (int pr = 0; pr < AHEAD; ++pr) vT[pr] = read_vT(pr);
+    fence();
+    // scaled scores, log2 domain; invisible keys -inf (only blocks that cross the
+    // diagonal or the end of the keys are masked)
+    float s2[4][kNT][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s2[kt][qt][r] = sT[kt][qt][r] * sl2;
+    if (!full) {
+      asm volatile("");   // keeps the masking inside the branch (no speculation into full blocks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < kNT; ++qt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = jb + 16 * kt + 4 * lg + r, i = qw0 + 16 * qt + lc;
+            s2[kt][qt][r] = ((jj < Tk) & (!p.causal | (jj <= i + off))) ? s2[kt][qt][r] : -INFINITY;
+          }
+    }
+    // P as bf16 B operands (k = 32 keys, n = query): element e of operand c is key
+    // 32c + 4 lg + e (e < 4) or 32c + 16 + 4 lg + e - 4 (e >= 4).
+    bf16x8 pb[2][kNT];
+#pragma unroll
+    for (int qt = 0; qt < kNT; ++qt) {
+      float bm = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s2[kt][qt][r]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(mrun[qt], bm);
+      const float mref = mn == -INFINITY ? 0.f : mn;           // no visible key yet: every term is 0
+      const float a = __builtin_amdgcn_exp2f(mrun[qt] - mref);  // 0 while the maximum is -inf
+      lrun[qt] *= a;
+      lrnd[qt] *= a;
+#pragma unroll
+      for (int dt = 0; dt < kNDT; ++dt) acO[dt][qt] *= a;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s2[kt][qt][r] - mref);
+          const __bf16 eb = (__bf16)e;
+          lrun[qt] += e;
+          lrnd[qt] += (float)eb;
+          pb[kt >> 1][qt][4 * (kt & 1) + r] = eb;
+        }
+      mrun[qt] = mn;
+    }
+    fence();
+    // O^T += V^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (pr + AHEAD < NP) vT[(pr + AHEAD) % (AHEAD + 1)] = read_vT(pr + AHEAD);
+      if (pr == 0 || pr == NP / 2) dma(2 + (pr != 0));
+      fence();
+      const int dt = pr >> 1, c = pr & 1;
+#pragma unroll
+      for (int qt = 0; qt < kNT; ++qt) mma(acO[dt][qt], vT[pr % (AHEAD + 1)], pb[c][qt]);
+      fence();
+    }
+  };
+
+  auto iteration = [&](int j, auto buf_c) {
+    constexpr int nxt = decltype(buf_c)::value ^ 1;
+    const int jb = j * BN;
+    wait_loads();
+    __syncthreads();   // block j is in LDS; every wave is done with block j - 1
+    const bool more = j + 1 < nblk;
+    auto dma = [&](int part) {
+      if (!more || part != 0) return;
+      kst.stage(sm_lds + (2 * nxt) * kTileBytes, Kh, p.sk[1], jb + BN, Tk);
+      vst.stage(sm_lds + (2 * nxt + 1) * kTileBytes, Vh, p.sv[1], jb + BN, Tk);
+    };
+    if (jb >= wkend) {
+      dma(0);
+      return;
+    }
+    const bool full = jb + BN <= Tk && (!p.causal || jb + BN - 1 <= qw0 + off);
+    block(buf_c, jb, full, dma);
+  };
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    iteration(j, BufC<0>{});
+    iteration(j + 1, BufC<1>{});
+  }
+  if (j < nblk) iteration(j, BufC<0>{});
+
+  // the four 16-lane groups hold disjoint key subsets of the same query
+#pragma unroll
+  for (int qt = 0; qt < kNT; ++qt) {
+    float l = lrun[qt], lr = lrnd[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    const int i = qw0 + 16 * qt + lc;
+    if (i < Tq) {
+      if (lg == 0 && p.lse_out) p.lse_out[rowbase + i] = (mrun[qt] + log2f(l)) * kLn2;
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      // the lane holds d = 16 dt + 4 lg + r of query i
+      const int64_t o = (int64_t)b * p.sdq[0] + (int64_t)i * p.sdq[1] + (int64_t)h * p.sdq[2] + 4 * lg;
+#pragma unroll
+      for (int dt = 0; dt < kNDT; ++dt) {
+        const f32x4 v4 = acO[dt][qt];
+        store4(p.dq, p.out_bf16, o + 16 * dt, v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ dkdv
 // Workgroup: kW * 16 * kNT keys of one kv-head; wave w owns kNT 16-key tiles starting
 // at kw0, K and V in registers as B operands. For every (q-head of the group, 64-query
@@ -614,6 +821,18 @@ bool mfma_path_applicable(const AttnParams& p) {
   // The staging loads address a 64-row block with 32-bit byte offsets from its first row.
   auto small = [](int64_t st) { return st >= 1 && st <= (int64_t)1 << 24; };
   return p.in_bf16 && p.D == kHD && small(p.sq[1]) && small(p.sk[1]) && small(p.sv[1]) && small(p.sdo[1]);
+}
+
+bool mfma_fwd_applicable(const AttnParams& p) {
+  auto small = [](int64_t st) { return st >= 1 && st <= (int64_t)1 << 24; };
+  return p.in_bf16 && p.D == kHD && small(p.sq[1]) && small(p.sk[1]) && small(p.sv[1]);
+}
+
+hipError_t launch_mfma_fwd(const AttnParams& p, hipStream_t s, KernelEvents ev) {
+  constexpr int BM = kW * 16 * kNT;
+  const dim3 grid(p.B * p.Hq, (p.Tq + BM - 1) / BM);
+  launch_kernel(fwd_mfma_kernel, grid, dim3(kT), 0, s, ev, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev) {

@@ -59,6 +59,9 @@ hipError_t launch_flash_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev
 // blocks. The dq pass takes a given lse (single sweep; writes dQ and D); the dk/dv pass
 // takes lse and D from the workspace or the caller, like launch_flash_dkdv.
 bool mfma_path_applicable(const AttnParams& p);
+// MFMA forward (bf16, D = 128): O and lse by online softmax, O written through dq / sdq.
+bool mfma_fwd_applicable(const AttnParams& p);
+hipError_t launch_mfma_fwd(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 
