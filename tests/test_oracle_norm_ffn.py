@@ -3,6 +3,7 @@ values, central differences of the forwards, and the invariants the formulas fix
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import norm_ffn as NF
 from oracle import verify
@@ -69,3 +70,85 @@ def test_relu2_mul_matches_central_differences():
     nu = verify.numerical_grad(lambda z: float(np.sum(dh * NF.relu2_mul_forward(g, z))), u, eps=1e-6)
     np.testing.assert_allclose(dg, ng, rtol=1e-7, atol=1e-8)
     np.testing.assert_allclose(du, nu, rtol=1e-7, atol=1e-8)
+
+
+# ----------------------------------------------------------------------------- FFN block
+
+def _tiny_ffn(seed, T=3, C=6, F=5, kink_free=True):
+    rng = np.random.default_rng(seed)
+    p = dict(x=rng.standard_normal((T, C)), gamma1=rng.uniform(0.5, 1.5, C),
+             w_gu=rng.standard_normal((C, 2 * F)) * 0.5, gamma2=rng.uniform(0.5, 1.5, F),
+             w_down=rng.standard_normal((F, C)) * 0.5)
+    if kink_free:   # keep every gate away from ReLU's kink so central differences apply
+        _, sv = NF.ffn_forward(**p)
+        assert np.min(np.abs(sv["gu"][:, :F])) > 1e-3
+    return p
+
+
+def _ffn_out(p, **over):
+    q = dict(p, **over)
+    return NF.ffn_forward(q["x"], q["gamma1"], q["w_gu"], q["gamma2"], q["w_down"])[0]
+
+
+def test_ffn_backward_matches_central_differences():
+    p = _tiny_ffn(11)
+    dout = np.random.default_rng(12).standard_normal(p["x"].shape)
+    _, sv = NF.ffn_forward(**p)
+    dx, dwgu, dwd = NF.ffn_backward(sv, dout)
+    for name, got in (("x", dx), ("w_gu", dwgu), ("w_down", dwd)):
+        num = verify.numerical_grad(lambda z: float(np.sum(dout * _ffn_out(p, **{name: z}))), p[name], eps=1e-6)
+        np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_ffn_backward_matches_torch_autograd():
+    # an independent statement of the same forward in torch float64 ops
+    p = _tiny_ffn(13, T=4, C=8, F=6)
+    dout = np.random.default_rng(14).standard_normal(p["x"].shape)
+    _, sv = NF.ffn_forward(**p)
+    dx, dwgu, dwd = NF.ffn_backward(sv, dout)
+    t = {k: torch.tensor(v, requires_grad=k in ("x", "w_gu", "w_down")) for k, v in p.items()}
+
+    def rms(z, g):
+        return z * g / torch.sqrt((z * z).mean(dim=1, keepdim=True) + 1e-6)
+
+    gu = rms(t["x"], t["gamma1"]) @ t["w_gu"]
+    F = gu.shape[1] // 2
+    h = torch.relu(gu[:, :F]) ** 2 * gu[:, F:]
+    out = t["x"] + rms(h, t["gamma2"]) @ t["w_down"]
+    (out * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(dx, t["x"].grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dwgu, t["w_gu"].grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dwd, t["w_down"].grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_ffn_backward_all_gates_closed_is_the_residual():
+    # every gate <= 0: h = 0, so hn = 0 and the ReLU passes no gradient: dx = dout exactly,
+    # and both weight gradients vanish
+    p = _tiny_ffn(15, kink_free=False)
+    p["w_gu"][:, :5] = -np.abs(p["w_gu"][:, :5])
+    p["x"] = np.abs(p["x"])
+    _, sv = NF.ffn_forward(**p)
+    assert np.all(sv["gu"][:, :5] <= 0)
+    dout = np.random.default_rng(16).standard_normal(p["x"].shape)
+    dx, dwgu, dwd = NF.ffn_backward(sv, dout)
+    np.testing.assert_array_equal(dx, dout)
+    np.testing.assert_array_equal(dwgu, 0.0)
+    np.testing.assert_array_equal(dwd, 0.0)
+
+
+def test_ffn_planted_mistakes_fail_the_difference_check(monkeypatch):
+    # plausible slips in the oracle's FFN backward must each break agreement with central
+    # differences: dUp and dGate swapped, no residual, sub-norm backward skipped
+    p = _tiny_ffn(17)
+    dout = np.random.default_rng(18).standard_normal(p["x"].shape)
+    _, sv = NF.ffn_forward(**p)
+    num = verify.numerical_grad(lambda z: float(np.sum(dout * _ffn_out(p, x=z))), p["x"], eps=1e-6)
+    good = NF.ffn_backward(sv, dout)[0]
+    assert np.max(np.abs(good - num)) < 1e-6
+    real = NF.relu2_mul_backward
+    monkeypatch.setattr(NF, "relu2_mul_backward", lambda g, u, d: real(g, u, d)[::-1])
+    assert np.max(np.abs(NF.ffn_backward(sv, dout)[0] - num)) > 1e-3
+    monkeypatch.setattr(NF, "relu2_mul_backward", real)
+    assert np.max(np.abs((NF.ffn_backward(sv, dout)[0] - dout) - num)) > 1e-3
+    monkeypatch.setattr(NF, "rmsnorm_backward_rows", lambda x, g, dy, eps=1e-6: np.asarray(dy, np.float64))
+    assert np.max(np.abs(NF.ffn_backward(sv, dout)[0] - num)) > 1e-3
