@@ -161,6 +161,28 @@ int rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const 
                          vtb_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * LayerNorm (no affine) backward: DaisyChain-Train transformer.js page, functions lnFwd /
+ * lnBwd ("layernorm (no affine)"). The forward keeps, per row of n values,
+ *     sigma = sqrt(mean((x - mean x)^2) + 1e-5),   y = (x - mean x) / sigma,
+ * and the backward is, from dy, y and sigma alone,
+ *     dx = (dy - mean(dy) - y * mean(dy * y)) / sigma.
+ * dtype VTB_F32 or VTB_BF16 is the storage type of dy, y and dx ([rows, n] contiguous);
+ * sig is fp32 [rows]. Arithmetic is fp32. dx must not overlap any input.
+ * -------------------------------------------------------------------------------------*/
+int layernorm_bwd(int32_t dtype, const void* dy, const void* y, const float* sig, void* dx, int32_t rows,
+                  int32_t n, vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ReLU^2 x Mul backward (the FFN gate): Hesper pull-request commit log, "FFN backward"
+ * (FFNBackward.lean). For h = ReLU(gate)^2 * up elementwise,
+ *     dgate = dh * up * 2 * ReLU(gate),   dup = dh * ReLU(gate)^2.
+ * gate, up, dh, dgate, dup: n contiguous elements of dtype (VTB_F32 or VTB_BF16);
+ * arithmetic is fp32. Outputs must not overlap inputs or each other.
+ * -------------------------------------------------------------------------------------*/
+int relu2_mul_bwd(int32_t dtype, const void* gate, const void* up, const void* dh, void* dgate, void* dup,
+                  int64_t n, vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Linear backward of Y = X W (Hesper commit log: outer-product dW and transposed dX;
  * transformer.js `backward`, Wo: gWo = ctxOut^T dx2, dctx = dx2 Wo^T):
  *     dX = dY W^T   [T, K]        dW = X^T dY = sum_t x_t (outer) dy_t   [K, N]
@@ -198,6 +220,37 @@ size_t layer_bwd_workspace_size(const layer_bwd_cfg* cfg);
 int layer_bwd(const layer_bwd_cfg* cfg, const layer_saved* saved, const float* dh_out,
               float* dh_in, float* dw, float* dk, float* dv, void* workspace,
               size_t workspace_bytes, vtb_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * One FFN block's backward: the Hesper pull-request commit log, "FFN backward"
+ * (FFNBackward.lean), ops in its order: ffnDown transpose, ffnSubNorm (RMSNorm) backward,
+ * ReLU^2 x Mul backward, ffnGate/Up transposes, ffnNorm (RMSNorm) backward; the residual
+ * passes dout through. The block's forward is read as
+ *     xn = RMSNorm(x; gamma1),  gu = xn Wgu  (Wgu = [Wgate | Wup], [C, 2F]),
+ *     h = ReLU(gu[:, :F])^2 * gu[:, F:],  hn = RMSNorm(h; gamma2),  out = x + hn Wdown,
+ * and the backward computes
+ *     dhn, dWdown = dout Wdown^T, hn^T dout
+ *     dgate, dup  = ReLU^2 x Mul backward(gate, up, RMSNormBackward(h, gamma2, dhn))
+ *     dxn, dWgu   = [dgate | dup] Wgu^T, xn^T [dgate | dup]
+ *     dx          = dout + RMSNormBackward(x, gamma1, dxn)
+ * with h formed again from the saved gate and up. Saved tensors (fp32, row-major,
+ * 16-byte aligned): x, xn [T, C]; gamma1 [C]; w_gu [C, 2F]; gu [T, 2F]; gamma2 [F];
+ * hn [T, F]; w_down [F, C]. Outputs: dx [T, C], dw_gu [C, 2F], dw_down [F, C]. dx == dout
+ * is allowed; no other overlap. Workspace from ffn_bwd_workspace_size().
+ * -------------------------------------------------------------------------------------*/
+typedef struct {
+  int32_t T, C, F;
+  float eps;
+} ffn_bwd_cfg;
+
+typedef struct {
+  const float *x, *gamma1, *xn, *w_gu, *gu, *gamma2, *hn, *w_down;
+} ffn_saved;
+
+size_t ffn_bwd_workspace_size(const ffn_bwd_cfg* cfg);
+
+int ffn_bwd(const ffn_bwd_cfg* cfg, const ffn_saved* saved, const float* dout, float* dx, float* dw_gu,
+            float* dw_down, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,4 +25,7 @@ from .gen import (  # noqa: F401
     layer_upstream_grad,
     long_causal_inputs,
     attention_inputs,
+    layernorm_inputs,
+    relu2_inputs,
+    ffn_inputs,
 )

@@ -160,3 +160,31 @@ def layer_upstream_grad(T=256, H=20, d=128, seed=1004):
     """The gradient arriving at the top of the layer stack, N(0, 1)."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 1_000_000]))
     return normal(rng, (T, H * d))
+
+
+def layernorm_inputs(rows: int, n: int, dtype: str = "f32", seed: int = 1006):
+    """LayerNorm rows x and upstream gradient dy, N(0, 1) with a per-row offset and scale
+    (x = 0.5 + 2 z) so the forward's centring and scaling both matter."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (rows, n), std=2.0, dtype="f32") + np.float32(0.5)
+    dy = normal(rng, (rows, n), dtype=dtype)
+    return dict(x=_store(x.astype(np.float64), dtype), dy=dy)
+
+
+def relu2_inputs(n: int, dtype: str = "f32", seed: int = 1007):
+    """gate, up, dh for the ReLU^2 x Mul gate: all N(0, 1), so about half the gates are closed."""
+    rng = np.random.default_rng(seed)
+    return dict(gate=normal(rng, (n,), dtype=dtype), up=normal(rng, (n,), dtype=dtype), dh=normal(rng, (n,), dtype=dtype))
+
+
+def ffn_inputs(T: int = 256, C: int = 2560, F: int = 6912, seed: int = 1008):
+    """One FFN block's parameters and input: x, dout N(0, 1); gamma1, gamma2 U(0.5, 1.5);
+    Wgu [C, 2F] and Wdown [F, C] N(0, 0.02 std). fp32."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (T, C))
+    gamma1 = uniform(rng, (C,), 0.5, 1.5)
+    w_gu = normal(rng, (C, 2 * F), std=0.02)
+    gamma2 = uniform(rng, (F,), 0.5, 1.5)
+    w_down = normal(rng, (F, C), std=0.02)
+    dout = normal(rng, (T, C))
+    return dict(x=x, gamma1=gamma1, w_gu=w_gu, gamma2=gamma2, w_down=w_down, dout=dout)

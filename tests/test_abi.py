@@ -104,3 +104,27 @@ def test_layer_validation_codes():
     cfg = vtb.make_layer_cfg(8, 2, 64, 0.1)
     assert L.layer_bwd(ctypes.byref(cfg), None, A0, A1, A2, A3, A4, WS, 1 << 30, None) == 1
     assert vtb.layer_bwd_workspace_size(cfg) > 0
+
+
+def test_norm_ffn_validation_codes():
+    L = vtb.lib()
+    assert L.layernorm_bwd(7, A0, A1, A2, A3, 4, 64, None) == 1                    # dtype
+    assert L.layernorm_bwd(0, A0, A1, A2, A3, 4, 0, None) == 1                     # n = 0
+    assert L.layernorm_bwd(0, A0, A1, A2, A0 + 16, 4, 64, None) == 3               # dx overlaps dy
+    assert L.layernorm_bwd(1, A0, A1, A2, A3, 0, 64, None) == 0                    # no rows: nothing to do
+    assert L.relu2_mul_bwd(0, A0, A1, A2, A3, A3 + 8, 64, None) == 3               # dgate overlaps dup
+    assert L.relu2_mul_bwd(0, A0, A1, A2, A1, A4, 64, None) == 3                   # dgate overlaps up
+    assert L.relu2_mul_bwd(0, A0, A1, A2, A3, A4, -1, None) == 1
+    assert L.relu2_mul_bwd(0, A0, A1, A2, A3, A4, 0, None) == 0
+    cfg = vtb.make_ffn_cfg(8, 64, 96)
+    need = vtb.ffn_bwd_workspace_size(cfg)
+    assert need > 0
+    sv = vtb.FfnSaved(A0, A1, A2, A3, A4, A5, A6, WS)
+    out = [WS + 0x1000000 * i for i in range(1, 5)]
+    assert L.ffn_bwd(ctypes.byref(cfg), ctypes.byref(sv), out[0], out[1], out[2], out[3], out[3] + 0x800000, 16, None) == 4
+    assert L.ffn_bwd(ctypes.byref(cfg), ctypes.byref(sv), out[0], A0, out[2], out[3], out[3] + 0x800000, need, None) == 3
+    assert L.ffn_bwd(ctypes.byref(cfg), None, out[0], out[1], out[2], out[3], out[3] + 0x800000, need, None) == 1
+    assert L.ffn_bwd(ctypes.byref(cfg), ctypes.byref(sv), out[0], out[1] + 4, out[2], out[3], out[3] + 0x800000, need,
+                     None) == 2                                                     # misaligned dx
+    bad = vtb.make_ffn_cfg(8, 64, 0)
+    assert L.ffn_bwd(ctypes.byref(bad), ctypes.byref(sv), out[0], out[1], out[2], out[3], out[3] + 0x800000, need, None) == 1

@@ -27,8 +27,8 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
     "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd", "attn_fwd_lse",
-    "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd",
-    "layer_bwd_workspace_size", "layer_bwd",
+    "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd", "relu2_mul_bwd",
+    "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
 )
 
 
@@ -62,6 +62,17 @@ class LayerSaved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("x", "gamma", "w", "o", "q", "k", "v", "P")]
 
 
+class FfnBwdCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("C", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+FFN_SAVED = ("x", "gamma1", "xn", "w_gu", "gu", "gamma2", "hn", "w_down")
+
+
+class FfnSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in FFN_SAVED]
+
+
 _lib = None
 
 
@@ -88,8 +99,12 @@ def lib() -> ctypes.CDLL:
         "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
         "rope_rmsnorm_res_bwd": (ctypes.c_int, [P, F32, P, P, P, P, I32, I32, I32, I32, F64, I32, F32, P]),
         "linear_bwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
+        "layernorm_bwd": (ctypes.c_int, [I32, P, P, P, P, I32, I32, P]),
+        "relu2_mul_bwd": (ctypes.c_int, [I32, P, P, P, P, P, I64, P]),
         "layer_bwd_workspace_size": (SZ, [ctypes.POINTER(LayerBwdCfg)]),
         "layer_bwd": (ctypes.c_int, [ctypes.POINTER(LayerBwdCfg), ctypes.POINTER(LayerSaved), P, P, P, P, P, P, SZ, P]),
+        "ffn_bwd_workspace_size": (SZ, [ctypes.POINTER(FfnBwdCfg)]),
+        "ffn_bwd": (ctypes.c_int, [ctypes.POINTER(FfnBwdCfg), ctypes.POINTER(FfnSaved), P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -250,6 +265,38 @@ def rope_rmsnorm_res_bwd(dq, x, gamma, dh_out, n_heads: int, head_dim: int, dq_s
     return dh_in
 
 
+def layernorm_bwd(dy, y, sig, dx=None, stream=None):
+    """lnBwd per row of dy, y [rows, n] (fp32 or bf16, contiguous) with the forward's sigma [rows] (fp32)."""
+    if dy.dtype != y.dtype or not dy.is_contiguous() or not y.is_contiguous() or dy.shape != y.shape or dy.dim() != 2:
+        raise TypeError("dy and y must be contiguous [rows, n] of one dtype")
+    if sig.dtype != torch.float32 or not sig.is_contiguous() or sig.shape != (dy.shape[0],):
+        raise TypeError("sig must be contiguous float32 [rows]")
+    dx = torch.empty_like(dy) if dx is None else dx
+    if dx.dtype != dy.dtype or dx.shape != dy.shape or not dx.is_contiguous():
+        raise TypeError("dx must be contiguous and match dy")
+    rows, n = dy.shape
+    _check(lib().layernorm_bwd(_dtype_code(dy.dtype), _ptr(dy), _ptr(y), _ptr(sig), _ptr(dx), rows, n, _stream(stream)),
+           "layernorm_bwd")
+    return dx
+
+
+def relu2_mul_bwd(gate, up, dh, dgate=None, dup=None, stream=None):
+    """(dgate, dup) of h = ReLU(gate)^2 * up for the upstream dh (same shape and dtype, contiguous)."""
+    for t, nm in ((up, "up"), (dh, "dh")):
+        if t.dtype != gate.dtype or t.shape != gate.shape or not t.is_contiguous():
+            raise TypeError(f"{nm} must be contiguous and match gate")
+    if not gate.is_contiguous():
+        raise TypeError("gate must be contiguous")
+    dgate = torch.empty_like(gate) if dgate is None else dgate
+    dup = torch.empty_like(gate) if dup is None else dup
+    for t, nm in ((dgate, "dgate"), (dup, "dup")):
+        if t.dtype != gate.dtype or t.shape != gate.shape or not t.is_contiguous():
+            raise TypeError(f"{nm} must be contiguous and match gate")
+    _check(lib().relu2_mul_bwd(_dtype_code(gate.dtype), _ptr(gate), _ptr(up), _ptr(dh), _ptr(dgate), _ptr(dup),
+                               gate.numel(), _stream(stream)), "relu2_mul_bwd")
+    return dgate, dup
+
+
 def linear_bwd(x, w, dy, want_dx: bool = True, want_dw: bool = True, dx=None, dw=None, stream=None):
     """dX = dY W^T, dW = X^T dY for Y = X W (fp32 contiguous). Returns (dx, dw)."""
     for t, nm in ((x, "x"), (w, "w"), (dy, "dy")):
@@ -299,3 +346,37 @@ def layer_bwd(saved: dict, dh_out, scale: float, eps: float = 1e-6, rope_base: f
     _check(lib().layer_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dh_out), _ptr(dh_in), _ptr(dw), _ptr(dk), _ptr(dv),
                            _ptr(workspace), workspace.numel(), _stream(stream)), "layer_bwd")
     return dh_in, dw, dk, dv
+
+
+def make_ffn_cfg(T, C, F, eps=1e-6) -> FfnBwdCfg:
+    c = FfnBwdCfg()
+    c.T, c.C, c.F, c.eps = int(T), int(C), int(F), float(eps)
+    return c
+
+
+def ffn_bwd_workspace_size(cfg: FfnBwdCfg) -> int:
+    return int(lib().ffn_bwd_workspace_size(ctypes.byref(cfg)))
+
+
+def ffn_bwd(saved: dict, dout, eps: float = 1e-6, dx=None, dw_gu=None, dw_down=None, workspace=None, stream=None):
+    """One FFN block's backward over its saved tensors (x, gamma1, xn, w_gu, gu, gamma2,
+    hn, w_down; fp32 contiguous); returns (dx, dw_gu, dw_down)."""
+    for n in FFN_SAVED:
+        t = saved[n]
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"saved[{n!r}] must be contiguous float32")
+    if dout.dtype != torch.float32 or not dout.is_contiguous():
+        raise TypeError("dout must be contiguous float32")
+    T, C = saved["x"].shape
+    F = saved["w_down"].shape[0]
+    cfg = make_ffn_cfg(T, C, F, eps)
+    sv = FfnSaved(*[saved[n].data_ptr() for n in FFN_SAVED])
+    dx = torch.empty_like(dout) if dx is None else dx
+    dw_gu = torch.empty_like(saved["w_gu"]) if dw_gu is None else dw_gu
+    dw_down = torch.empty_like(saved["w_down"]) if dw_down is None else dw_down
+    need = ffn_bwd_workspace_size(cfg)
+    if workspace is None:
+        workspace = _workspace(need, dout.device)
+    _check(lib().ffn_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dout), _ptr(dx), _ptr(dw_gu), _ptr(dw_down),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)), "ffn_bwd")
+    return dx, dw_gu, dw_down

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libvtb.so")
 
-SOURCES = ["api.cpp", "attn_flash_bwd.hip", "attn_bwd_mfma.hip", "attn_decode.hip", "elementwise.hip", "gemm_f32.hip"]
+SOURCES = ["api.cpp", "attn_flash_bwd.hip", "attn_bwd_mfma.hip", "attn_decode.hip", "elementwise.hip", "gemm_f32.hip", "ffn_norm.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -386,6 +386,40 @@ int rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const 
                     "rope_rmsnorm_res_bwd");
 }
 
+int layernorm_bwd(int32_t dtype, const void* dy, const void* y, const float* sig, void* dx, int32_t rows, int32_t n,
+                  vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(dtype)) return fail(VTB_ERR_ARG, "dtype=%d", dtype);
+  if (rows < 0 || n < 1) return fail(VTB_ERR_ARG, "bad shape rows=%d n=%d", rows, n);
+  if (rows == 0) return VTB_OK;
+  if (!dy || !y || !sig || !dx) return fail(VTB_ERR_ARG, "dy, y, sig and dx must be non-NULL");
+  const size_t bytes = (size_t)rows * n * esize(dtype);
+  const Span o = span_of(dx, bytes);
+  if (overlap(o, span_of(dy, bytes)) || overlap(o, span_of(y, bytes)) || overlap(o, span_of(sig, (size_t)rows * 4)))
+    return fail(VTB_ERR_ALIAS, "dx overlaps an input");
+  return hip_status(vtb::launch_layernorm_bwd(dtype == VTB_BF16, dy, y, sig, dx, rows, n,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    "layernorm_bwd");
+}
+
+int relu2_mul_bwd(int32_t dtype, const void* gate, const void* up, const void* dh, void* dgate, void* dup, int64_t n,
+                  vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(dtype)) return fail(VTB_ERR_ARG, "dtype=%d", dtype);
+  if (n < 0) return fail(VTB_ERR_ARG, "n=%lld is negative", (long long)n);
+  if (n == 0) return VTB_OK;
+  if (!gate || !up || !dh || !dgate || !dup) return fail(VTB_ERR_ARG, "gate, up, dh, dgate and dup must be non-NULL");
+  const size_t bytes = (size_t)n * esize(dtype);
+  const Span sg = span_of(gate, bytes), su = span_of(up, bytes), sd = span_of(dh, bytes);
+  const Span og = span_of(dgate, bytes), ou = span_of(dup, bytes);
+  for (const Span& o : {og, ou})
+    if (overlap(o, sg) || overlap(o, su) || overlap(o, sd)) return fail(VTB_ERR_ALIAS, "an output overlaps an input");
+  if (overlap(og, ou)) return fail(VTB_ERR_ALIAS, "dgate overlaps dup");
+  return hip_status(vtb::launch_relu2_mul_bwd(dtype == VTB_BF16, gate, up, dh, dgate, dup, n,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    "relu2_mul_bwd");
+}
+
 int linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw, int32_t T, int32_t K, int32_t N,
                vtb_stream_t stream) {
   g_last_error.clear();
@@ -471,6 +505,72 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   return hip_status(vtb::launch_rope_rmsnorm_res_bwd(dq, 1.0f, sv->x, sv->gamma, dh_out, dh_in, T, H, D, 0,
                                                      c->rope_base, c->rope_layout, c->eps, s),
                     "layer rope/rmsnorm/residual");
+}
+
+
+size_t ffn_bwd_workspace_size(const ffn_bwd_cfg* c) {
+  if (!c || c->T < 1 || c->C < 1 || c->F < 1) return 0;
+  const size_t T = c->T, C = c->C, F = c->F;
+  // dhn [T, F], dgu [T, 2F], dxn [T, C], and the dX partials of either split contraction
+  const size_t parts = std::max((size_t)vtb::linear_bwd_splits(c->T, c->F, c->C) * T * F,
+                                (size_t)vtb::linear_bwd_splits(c->T, c->C, 2 * c->F) * T * C);
+  return align256(T * F * 4) + align256(T * 2 * F * 4) + align256(T * C * 4) + align256(parts * 4);
+}
+
+int ffn_bwd(const ffn_bwd_cfg* c, const ffn_saved* sv, const float* dout, float* dx, float* dw_gu, float* dw_down,
+            void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!c || !sv) return fail(VTB_ERR_ARG, "cfg and saved must be non-NULL");
+  if (c->T < 1 || c->C < 1 || c->F < 1) return fail(VTB_ERR_ARG, "T=%d C=%d F=%d must be >= 1", c->T, c->C, c->F);
+  if ((int64_t)c->C * 2 * c->F > (int64_t)1 << 31 || (int64_t)c->T * 2 * c->F > (int64_t)1 << 31)
+    return fail(VTB_ERR_UNSUPPORTED, "a tensor exceeds 2^31 elements");
+  if (!(c->eps >= 0.f) || !std::isfinite(c->eps)) return fail(VTB_ERR_ARG, "eps must be finite and >= 0");
+  const float* in_ptrs[9] = {sv->x, sv->gamma1, sv->xn, sv->w_gu, sv->gu, sv->gamma2, sv->hn, sv->w_down, dout};
+  for (const float* ptr : in_ptrs)
+    if (!ptr) return fail(VTB_ERR_ARG, "a saved tensor or dout is NULL");
+  if (!dx || !dw_gu || !dw_down) return fail(VTB_ERR_ARG, "outputs must be non-NULL");
+  for (const float* ptr : in_ptrs)
+    if (!aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (!aligned16(dx) || !aligned16(dw_gu) || !aligned16(dw_down) || !aligned16(workspace))
+    return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const int T = c->T, C = c->C, F = c->F;
+  const size_t TC = (size_t)T * C * 4, TF = (size_t)T * F * 4;
+  const size_t in_bytes[9] = {TC, (size_t)C * 4, TC, (size_t)C * 2 * F * 4, 2 * TF, (size_t)F * 4, TF, (size_t)F * C * 4, TC};
+  Span ins[9];
+  for (int i = 0; i < 9; ++i) ins[i] = span_of(in_ptrs[i], in_bytes[i]);
+  const Span sdx = span_of(dx, TC), sgu = span_of(dw_gu, (size_t)C * 2 * F * 4), sdn = span_of(dw_down, (size_t)F * C * 4);
+  for (int i = 0; i < 9; ++i) {
+    if (i != 8 && overlap(sdx, ins[i])) return fail(VTB_ERR_ALIAS, "dx overlaps saved tensor %d", i);
+    if (overlap(sgu, ins[i]) || overlap(sdn, ins[i])) return fail(VTB_ERR_ALIAS, "a weight gradient overlaps input %d", i);
+  }
+  if (dx != dout && overlap(sdx, ins[8])) return fail(VTB_ERR_ALIAS, "dx partially overlaps dout");
+  if (overlap(sdx, sgu) || overlap(sdx, sdn) || overlap(sgu, sdn)) return fail(VTB_ERR_ALIAS, "outputs overlap");
+  const size_t need = ffn_bwd_workspace_size(c);
+  if (!workspace || workspace_bytes < need)
+    return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+  const Span sws = span_of(workspace, need);
+  for (int i = 0; i < 9; ++i)
+    if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps input %d", i);
+  if (overlap(sws, sdx) || overlap(sws, sgu) || overlap(sws, sdn)) return fail(VTB_ERR_ALIAS, "workspace overlaps an output");
+
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(workspace);
+  float* dhn = reinterpret_cast<float*>(base);
+  float* dgu = reinterpret_cast<float*>(base + align256(TF));
+  float* dxn = reinterpret_cast<float*>(base + align256(TF) + align256(2 * TF));
+  float* part = reinterpret_cast<float*>(base + align256(TF) + align256(2 * TF) + align256(TC));
+
+  // 1. ffnDown transpose: dhn = dout Wdown^T, dWdown = hn^T dout
+  int rc = hip_status(vtb::launch_linear_bwd_split(sv->hn, sv->w_down, dout, dhn, dw_down, T, F, C, part, s), "ffn down");
+  if (rc) return rc;
+  // 2. ffnSubNorm backward fused with ReLU^2 x Mul backward: dgu = [dgate | dup]
+  rc = hip_status(vtb::launch_subnorm_relu2_bwd(sv->gu, dhn, sv->gamma2, dgu, T, F, c->eps, s), "ffn sub-norm/relu2");
+  if (rc) return rc;
+  // 3. ffnGate/Up transposes as one product: dxn = dgu Wgu^T, dWgu = xn^T dgu
+  rc = hip_status(vtb::launch_linear_bwd_split(sv->xn, sv->w_gu, dgu, dxn, dw_gu, T, C, 2 * F, part, s), "ffn gate/up");
+  if (rc) return rc;
+  // 4. ffnNorm backward plus the residual: dx = dout + RMSNormBackward(x, gamma1, dxn)
+  return hip_status(vtb::launch_rmsnorm_res_bwd(sv->x, sv->gamma1, dxn, dout, dx, T, C, c->eps, s), "ffn norm/residual");
 }
 
 }  // extern "C"

@@ -90,6 +90,22 @@ hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const fl
                                        int n_heads, int head_dim, int pos0, double base, int layout,
                                        float eps, hipStream_t s);
 
+// LayerNorm (no affine) backward from the forward's y and sigma, rows of n values, fp32 or
+// bf16 storage (bf16 != 0) with fp32 arithmetic; sigma is fp32.
+hipError_t launch_layernorm_bwd(int bf16, const void* dy, const void* y, const float* sig, void* dx, int rows, int n,
+                                hipStream_t s);
+// ReLU^2 x Mul backward over n elements, fp32 or bf16 storage.
+hipError_t launch_relu2_mul_bwd(int bf16, const void* gate, const void* up, const void* dh, void* dgate, void* dup,
+                                int64_t n, hipStream_t s);
+
+// FFN block pieces (fp32): the sub-norm backward fused with ReLU^2 x Mul backward over
+// [T, 2F] gate|up rows (dgu gets dgate|dup), and RMSNorm backward plus a residual
+// (dx = dres + RMSNormBackward(x, gamma, dy); dx == dres allowed).
+hipError_t launch_subnorm_relu2_bwd(const float* gu, const float* dhn, const float* gamma2, float* dgu, int T, int F,
+                                    float eps, hipStream_t s);
+hipError_t launch_rmsnorm_res_bwd(const float* x, const float* gamma, const float* dy, const float* dres, float* dx,
+                                  int T, int n, float eps, hipStream_t s);
+
 // fp32 MFMA GEMMs of the linear backward (one launch computes both products).
 hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw,
                              int T, int K, int N, hipStream_t s);
