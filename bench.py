@@ -152,7 +152,8 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd")
+EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd",
+               "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd")
 
 
 def extra_workloads(torch, vtb, hip, only=None):
@@ -259,6 +260,63 @@ def extra_workloads(torch, vtb, hip, only=None):
                               "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                            "algorithmic_bytes": byts}}
         del dq_, xx, dh, dh_in, dy3, dx3
+
+    def hbm_line(name, what, ms, byts):
+        out[name] = {"workload": what, "ms": round(ms, 5), "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                     "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes": byts}}
+
+    if want("layernorm_bwd"):
+        # LayerNorm (no affine) backward, 7680 x 2560: dy, y read, dx written, sigma per row
+        rows, n = 30 * 256, 2560
+        for dt, tdt, es in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+            inp = synth.layernorm_inputs(rows, n, dt)
+            x = up(inp["x"], dt).float()
+            mu = x.mean(1, keepdim=True)
+            sig = torch.sqrt(((x - mu) ** 2).mean(1) + 1e-5).contiguous()
+            y = ((x - mu) / sig[:, None]).to(tdt).contiguous()
+            dy, dx = up(inp["dy"], dt), torch.empty_like(y)
+            f = lambda: vtb.layernorm_bwd(dy, y, sig, dx=dx, stream=torch.cuda.current_stream())
+            ms = graph_ms(torch, hip, f, 20)
+            hbm_line("layernorm_bwd" + ("" if dt == "f32" else "_bf16"), f"LayerNorm backward, {rows} x {n} {dt}", ms,
+                     3 * rows * n * es + rows * 4)
+            del x, y, dy, dx, sig
+
+    if want("relu2_mul_bwd"):
+        # ReLU^2 x Mul backward over the FFN activations of 30 x 256 tokens x 6912: gate, up, dh read, dgate, dup written
+        n = 30 * 256 * 6912
+        gen = torch.Generator(device=dev).manual_seed(1007)
+        for tdt, es, tag in ((torch.float32, 4, "f32"), (torch.bfloat16, 2, "bf16")):
+            g, u, dh = (torch.randn(n, generator=gen, device=dev).to(tdt) for _ in range(3))
+            dg, du = torch.empty_like(g), torch.empty_like(g)
+            f = lambda: vtb.relu2_mul_bwd(g, u, dh, dgate=dg, dup=du, stream=torch.cuda.current_stream())
+            ms = graph_ms(torch, hip, f, 20)
+            hbm_line("relu2_mul_bwd" + ("" if tag == "f32" else "_bf16"), f"ReLU^2 x Mul backward, 7680 x 6912 {tag}", ms,
+                     5 * n * es)
+            del g, u, dh, dg, du
+
+    if want("ffn_bwd"):
+        # one FFN block's backward, T256 C2560 F6912 fp32; saved activations from a torch fp32 forward (setup only)
+        T, Cf, F = 256, 2560, 6912
+        p = synth.ffn_inputs(T, Cf, F)
+        x, g1, wgu, g2, wd, dout = (up(p[n]) for n in ("x", "gamma1", "w_gu", "gamma2", "w_down", "dout"))
+        rms = lambda z, g: z * torch.rsqrt((z * z).mean(1, keepdim=True) + 1e-6) * g
+        xn = rms(x, g1).contiguous()
+        gu = (xn @ wgu).contiguous()
+        hn = rms(torch.relu(gu[:, :F]) ** 2 * gu[:, F:], g2).contiguous()
+        saved = {"x": x, "gamma1": g1, "xn": xn, "w_gu": wgu, "gu": gu, "gamma2": g2, "hn": hn, "w_down": wd}
+        dx, dwgu, dwd = torch.empty_like(dout), torch.empty_like(wgu), torch.empty_like(wd)
+        fws = torch.empty(vtb.ffn_bwd_workspace_size(vtb.make_ffn_cfg(T, Cf, F)), dtype=torch.uint8, device=dev)
+        f = lambda: vtb.ffn_bwd(saved, dout, dx=dx, dw_gu=dwgu, dw_down=dwd, workspace=fws,
+                                stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 5)
+        fl = 12 * T * Cf * F
+        out["ffn_bwd"] = {"workload": "FFN block backward, T256 C2560 F6912 fp32 (gate/up/down GEMMs, norms, ReLU^2 x Mul)",
+                          "ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                          "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
+                                       "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                                       "algorithmic_flops": fl}}
+        del saved, x, xn, gu, hn, wgu, wd, dx, dwgu, dwd, fws
 
     if want("layer_chain"):
         # 30-layer chain: T256, hidden 2560 = 20 x 128, fp32, saved softmax P per layer

@@ -126,34 +126,49 @@ __device__ __forceinline__ void relu2_mul_grad(float g, float u, float d, float*
   *du = d * r * r;
 }
 
-// 16-byte vectors over [0, nvec), grid-stride; the scalar tail [nvec * W, n) is taken by
-// the first threads of the grid.
-template <typename E>
+// 16-byte vectors over [0, nvec): each thread takes U vectors per round, spaced one grid
+// apart, and issues all of their loads before any arithmetic; rounds repeat grid-stride.
+// The scalar tail [nvec * W, n) is taken by the first threads of the grid.
+template <typename E, int U>
 __global__ __launch_bounds__(256) void relu2_mul_bwd_vec_kernel(const E* __restrict__ gate, const E* __restrict__ up,
                                                                 const E* __restrict__ dh, E* __restrict__ dgate,
                                                                 E* __restrict__ dup, int64_t n) {
   using V = typename Vec16<E>::type;
   constexpr int W = Vec16<E>::n;
   const int64_t nvec = n / W;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t grid = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const V* g4 = reinterpret_cast<const V*>(gate);
   const V* u4 = reinterpret_cast<const V*>(up);
   const V* d4 = reinterpret_cast<const V*>(dh);
   V* og = reinterpret_cast<V*>(dgate);
   V* ou = reinterpret_cast<V*>(dup);
-  for (int64_t i = t0; i < nvec; i += stride) {
-    const V g = g4[i], u = u4[i], d = d4[i];
-    V rg, ru;
+  for (int64_t base = t0; base < nvec; base += U * grid) {
+    V g[U], u[U], d[U];
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      float a, b;
-      relu2_mul_grad(to_f32(g[k]), to_f32(u[k]), to_f32(d[k]), &a, &b);
-      rg[k] = from_f32<E>(a);
-      ru[k] = from_f32<E>(b);
+    for (int r = 0; r < U; ++r) {
+      const int64_t i = min(base + r * grid, nvec - 1);
+      g[r] = __builtin_nontemporal_load(&g4[i]);
+      u[r] = __builtin_nontemporal_load(&u4[i]);
+      d[r] = __builtin_nontemporal_load(&d4[i]);
     }
-    og[i] = rg;
-    ou[i] = ru;
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int64_t i = base + r * grid;
+      if (i < nvec) {
+        V rg, ru;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          float a, b;
+          relu2_mul_grad(to_f32(g[r][k]), to_f32(u[r][k]), to_f32(d[r][k]), &a, &b);
+          rg[k] = from_f32<E>(a);
+          ru[k] = from_f32<E>(b);
+        }
+        // streamed once: nontemporal stores keep the outputs from displacing the inputs in cache
+        __builtin_nontemporal_store(rg, &og[i]);
+        __builtin_nontemporal_store(ru, &ou[i]);
+      }
+    }
   }
   const int64_t j = nvec * W + t0;
   if (j < n) {
@@ -357,9 +372,10 @@ template <typename E>
 hipError_t relu2_mul_bwd_t(const E* gate, const E* up, const E* dh, E* dgate, E* dup, int64_t n, hipStream_t s) {
   constexpr int W = Vec16<E>::n;
   if (al16(gate) && al16(up) && al16(dh) && al16(dgate) && al16(dup)) {
+    // four vectors per thread per round, at most 8192 workgroups (larger inputs take more rounds)
     const int64_t units = std::max<int64_t>(n / W, 1);
-    const int grid = (int)std::min<int64_t>((units + 255) / 256, 4096);
-    hipLaunchKernelGGL(relu2_mul_bwd_vec_kernel<E>, dim3(grid), dim3(256), 0, s, gate, up, dh, dgate, dup, n);
+    const int grid = (int)std::min<int64_t>((units + 1023) / 1024, 8192);
+    hipLaunchKernelGGL((relu2_mul_bwd_vec_kernel<E, 4>), dim3(grid), dim3(256), 0, s, gate, up, dh, dgate, dup, n);
   } else {
     const int grid = (int)std::min<int64_t>((n + 255) / 256, 4096);
     hipLaunchKernelGGL(relu2_mul_bwd_any_kernel<E>, dim3(grid), dim3(256), 0, s, gate, up, dh, dgate, dup, n);
