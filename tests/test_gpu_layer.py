@@ -45,6 +45,25 @@ def test_rope_positions_layouts_inplace(layout):
     assert_close("rope_inplace", host(x), ref, TOL["f32"])
 
 
+# (T, H, d, layout, pad): the float4 kernel with a padded token stride, and the per-pair
+# kernel (head_dim not a multiple of 4, or of 8 for the half-split layout)
+@pytest.mark.parametrize("T,H,d,layout,pad", [(29, 20, 128, 0, 4), (29, 4, 64, 1, 12), (11, 3, 6, 0, 0), (11, 3, 12, 1, 2),
+                                               (7, 64, 128, 1, 0), (5, 80, 128, 0, 0)])
+def test_rope_strided_and_scalar_paths(T, H, d, layout, pad):
+    need_gpu()
+    say(f"rope T {T} H {H} d {d} layout {layout} token pad {pad}")
+    rng = np.random.default_rng(T * 100 + d)
+    full = rng.standard_normal((T, H * d + pad)).astype(np.float32)
+    dy = full[:, : H * d].reshape(T, H, d)
+    ref = L.rope_backward_rows(dy, np.arange(T) + 3, 10000.0, layout)
+    buf = dev(full)
+    dyv = buf[:, : H * d].view(T, H, d) if pad == 0 else buf.as_strided((T, H, d), (H * d + pad, d, 1))
+    dxv = torch.zeros_like(buf).as_strided((T, H, d), (H * d + pad, d, 1))
+    vtb.rope_bwd(dyv, pos0=3, layout=layout, dx=dxv)
+    torch.cuda.synchronize()
+    assert_close("rope", host(dxv), ref, TOL["f32"])
+
+
 @pytest.mark.parametrize("rows,n", [(3, 64), (17, 2560), (5, 5000), (4, 100)])
 def test_rmsnorm_shapes(rows, n):
     need_gpu()

@@ -26,6 +26,12 @@ __device__ __forceinline__ void rope_sincos(double theta, float* s, float* c) {
   sincosf((float)red, s, c);
 }
 
+// A float4 store that bypasses cache retention (written once, never read back here).
+__device__ __forceinline__ void nt_store4(float4* p, const float4& v) {
+  const f32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
+
 // Sum two values over the whole block (blockDim.x == 256).
 __device__ __forceinline__ float2 block_sum2(float a, float b) {
   __shared__ float red[2][8];
@@ -73,6 +79,70 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(const float* dy, float* d
   }
 }
 
+// Vector form: one 256-thread workgroup per token, float4 moves. Every load of the token's
+// row is issued first; meanwhile the first head_dim/2 threads put the token's (cos, sin)
+// per frequency into LDS (angle formed and reduced in fp64, sin/cos in fp32), so each
+// angle is computed once per token and shared by all heads.
+// LAYOUT 0 pairs (2i, 2i+1): a float4 holds two pairs. LAYOUT 1 pairs (i, i + d/2): a unit
+// is the float4 at i and the float4 at i + d/2 of the same head, four pairs.
+// dx == dy is allowed: a thread stores only what it loaded itself, after the barrier.
+template <int LAYOUT, int NV>
+__global__ __launch_bounds__(256) void rope_bwd_vec_kernel(const float4* dy, float4* dx, int n_heads, int hd,
+                                                           int64_t tok_stride4, const int32_t* __restrict__ pos,
+                                                           int pos0, double log2_base) {
+  extern __shared__ float2 cs[];   // [hd / 2] (cos, sin)
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int hd4 = hd / 4, C4 = n_heads * hd4;
+  const int units = LAYOUT == 0 ? C4 : C4 / 2;
+  const int64_t ro = (int64_t)t * tok_stride4;
+  float4 a[NV], b[NV];
+  int ia[NV], ib[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int u = min(tid + 256 * e, units - 1);
+    if (LAYOUT == 0) {
+      ia[e] = ib[e] = u;
+    } else {
+      const int h = u / (hd4 / 2), j = u % (hd4 / 2);
+      ia[e] = h * hd4 + j;
+      ib[e] = ia[e] + hd4 / 2;
+    }
+    a[e] = dy[ro + ia[e]];
+    if (LAYOUT == 1) b[e] = dy[ro + ib[e]];
+  }
+  const double pp = pos ? (double)pos[t] : (double)pos0 + t;
+  for (int i = tid; i < hd / 2; i += 256) {
+    float sn, cn;
+    rope_sincos(pp * exp2(-(2.0 * i / hd) * log2_base), &sn, &cn);
+    cs[i] = make_float2(cn, sn);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    if (tid + 256 * e >= units) continue;
+    if (LAYOUT == 0) {
+      const int i0 = ((4 * ia[e]) % hd) / 2;
+      const float2 c0 = cs[i0], c1 = cs[i0 + 1];
+      const float4 y = a[e];
+      const float4 r = make_float4(y.x * c0.x + y.y * c0.y, -y.x * c0.y + y.y * c0.x, y.z * c1.x + y.w * c1.y,
+                                   -y.z * c1.y + y.w * c1.x);
+      nt_store4(&dx[ro + ia[e]], r);
+    } else {
+      const int i0 = 4 * (ia[e] % hd4);
+      const float ya[4] = {a[e].x, a[e].y, a[e].z, a[e].w}, yb[4] = {b[e].x, b[e].y, b[e].z, b[e].w};
+      float ra[4], rb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 c = cs[i0 + k];
+        ra[k] = ya[k] * c.x + yb[k] * c.y;
+        rb[k] = -ya[k] * c.y + yb[k] * c.x;
+      }
+      nt_store4(&dx[ro + ia[e]], make_float4(ra[0], ra[1], ra[2], ra[3]));
+      nt_store4(&dx[ro + ib[e]], make_float4(rb[0], rb[1], rb[2], rb[3]));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------- RMSNorm backward
 // One 256-thread block per row; a row of up to 256*MAXE values stays in registers.
 template <int MAXE>
@@ -103,7 +173,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
     const int idx = threadIdx.x + 256 * e;
-    if (idx < n) dx[row * n + idx] = (gv[e] - xv[e] * coef) * rinv;
+    if (idx < n) __builtin_nontemporal_store((gv[e] - xv[e] * coef) * rinv, &dx[row * n + idx]);
   }
 }
 
@@ -282,8 +352,8 @@ __global__ __launch_bounds__(256) void rope_rmsnorm_res_vec_kernel(const float4*
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
     if (tid + 256 * e < units) {
-      dh_in[ro + ia[e]] = out(qa[e], ga[e], xa[e], ha[e]);
-      if (LAYOUT == 1) dh_in[ro + ib[e]] = out(qb[e], gb[e], xb[e], hb[e]);
+      nt_store4(&dh_in[ro + ia[e]], out(qa[e], ga[e], xa[e], ha[e]));
+      if (LAYOUT == 1) nt_store4(&dh_in[ro + ib[e]], out(qb[e], gb[e], xb[e], hb[e]));
     }
   }
 }
@@ -312,6 +382,31 @@ int grid_for(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>((n 
 
 hipError_t launch_rope_bwd(const float* dy, float* dx, int n_tok, int n_heads, int head_dim, int64_t tok_stride,
                            const int32_t* pos, int pos0, double base, int layout, hipStream_t s) {
+  const int64_t C = (int64_t)n_heads * head_dim;
+  const bool vec = (layout == 0 ? head_dim % 4 == 0 : head_dim % 8 == 0) && tok_stride % 4 == 0 && C / 4 <= 256 * 8 &&
+                   ((uintptr_t)dy | (uintptr_t)dx) % 16 == 0;
+  if (vec) {
+    const int units = (int)(layout == 0 ? C / 4 : C / 8);
+    const int nv = (units + 255) / 256;
+    const size_t lds = (size_t)(head_dim / 2) * sizeof(float2);
+    const double l2b = std::log2(base);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(n_tok), dim3(256), lds, s, reinterpret_cast<const float4*>(dy),
+                         reinterpret_cast<float4*>(dx), n_heads, head_dim, tok_stride / 4, pos, pos0, l2b);
+    };
+    if (layout == 0) {
+      if (nv <= 1) go(rope_bwd_vec_kernel<0, 1>);
+      else if (nv <= 2) go(rope_bwd_vec_kernel<0, 2>);
+      else if (nv <= 4) go(rope_bwd_vec_kernel<0, 4>);
+      else go(rope_bwd_vec_kernel<0, 8>);
+    } else {
+      if (nv <= 1) go(rope_bwd_vec_kernel<1, 1>);
+      else if (nv <= 2) go(rope_bwd_vec_kernel<1, 2>);
+      else if (nv <= 4) go(rope_bwd_vec_kernel<1, 4>);
+      else go(rope_bwd_vec_kernel<1, 8>);
+    }
+    return hipGetLastError();
+  }
   const int64_t items = (int64_t)n_tok * (head_dim / 2);
   hipLaunchKernelGGL(rope_bwd_kernel, dim3(grid_for(items)), dim3(256), 0, s, dy, dx, n_tok, n_heads, head_dim, tok_stride,
                      pos, pos0, base, layout);

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_vec_kernel(const E* __restr
       V o;
 #pragma unroll
       for (int k = 0; k < W; ++k) o[k] = from_f32<E>((to_f32(a[e][k]) - mdy - to_f32(b[e][k]) * mdyy) * rs);
-      dxr[u] = o;
+      __builtin_nontemporal_store(o, &dxr[u]);
     }
   }
 }
@@ -250,8 +250,8 @@ __global__ __launch_bounds__(256) void subnorm_relu2_bwd_vec_kernel(const f32x4*
         og[k] = a;
         ou[k] = b;
       }
-      orow[c] = og;
-      orow[F4 + c] = ou;
+      __builtin_nontemporal_store(og, &orow[c]);
+      __builtin_nontemporal_store(ou, &orow[F4 + c]);
     }
   }
 }
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void rmsnorm_res_bwd_vec_kernel(const f32x4* _
       f32x4 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] = rv[e][k] + (gy[e][k] - xv[e][k] * coef) * rinv;
-      dx[t * n4 + c] = o;
+      __builtin_nontemporal_store(o, &dx[t * n4 + c]);
     }
   }
 }
