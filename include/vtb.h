@@ -252,6 +252,39 @@ size_t ffn_bwd_workspace_size(const ffn_bwd_cfg* cfg);
 int ffn_bwd(const ffn_bwd_cfg* cfg, const ffn_saved* saved, const float* dout, float* dx, float* dw_gu,
             float* dw_down, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * One transformer attention block's backward, as the DaisyChain-Train transformer.js page
+ * builds the block (forward layer loop and `backward`): over B sequences of T tokens,
+ * hidden C = H * D,
+ *     ln = LayerNorm(xin) (no affine; y, sigma kept),  [q | k | v] = ln.y Wqkv  (Wqkv =
+ *     [Wq | Wk | Wv], [C, 3C]),  P = causal softmax(scale q_h k_h^T) per sequence and head,
+ *     ctx = P v_h,  x2 = xin + ctx Wo,
+ * and the backward from dx2:
+ *     gWo, dctx  = ctx^T dx2, dx2 Wo^T
+ *     dq, dk, dv = attention backward with the saved P (dS = P o (dP - rowsum(P o dP)))
+ *     gWqkv, dln = ln.y^T [dq | dk | dv], [dq | dk | dv] Wqkv^T
+ *     dx         = dx2 + lnBwd(dln, ln.y, sigma)
+ * Saved tensors (fp32, row-major, 16-byte aligned): ln_y [B T, C], ln_sig [B T],
+ * w_qkv [C, 3C], qkv [B T, 3C] (q, k, v side by side, head h at columns h D of each
+ * third), P [B H, T, T], ctx [B T, C], w_o [C, C]. Outputs: dx [B T, C], dw_qkv [C, 3C],
+ * dw_o [C, C]. dx == dx2 is allowed; no other overlap. Workspace from
+ * attn_block_bwd_workspace_size().
+ * -------------------------------------------------------------------------------------*/
+typedef struct {
+  int32_t B, T, H, D;
+  float scale;
+  int32_t causal;
+} attn_block_cfg;
+
+typedef struct {
+  const float *ln_y, *ln_sig, *w_qkv, *qkv, *P, *ctx, *w_o;
+} attn_block_saved;
+
+size_t attn_block_bwd_workspace_size(const attn_block_cfg* cfg);
+
+int attn_block_bwd(const attn_block_cfg* cfg, const attn_block_saved* saved, const float* dx2, float* dx,
+                   float* dw_qkv, float* dw_o, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,4 +28,5 @@ from .gen import (  # noqa: F401
     layernorm_inputs,
     relu2_inputs,
     ffn_inputs,
+    block_inputs,
 )

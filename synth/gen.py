@@ -188,3 +188,15 @@ def ffn_inputs(T: int = 256, C: int = 2560, F: int = 6912, seed: int = 1008):
     w_down = normal(rng, (F, C), std=0.02)
     dout = normal(rng, (T, C))
     return dict(x=x, gamma1=gamma1, w_gu=w_gu, gamma2=gamma2, w_down=w_down, dout=dout)
+
+
+def block_inputs(B: int = 1, T: int = 256, H: int = 20, d: int = 128, seed: int = 1009):
+    """One attention block's input and weights: xin, dx2 N(0, 1); Wqkv [C, 3C] and Wo [C, C]
+    N(0, 0.02 std). fp32."""
+    rng = np.random.default_rng(seed)
+    C = H * d
+    xin = normal(rng, (B * T, C))
+    w_qkv = normal(rng, (C, 3 * C), std=0.02)
+    w_o = normal(rng, (C, C), std=0.02)
+    dx2 = normal(rng, (B * T, C))
+    return dict(xin=xin, w_qkv=w_qkv, w_o=w_o, dx2=dx2)

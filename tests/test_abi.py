@@ -128,3 +128,20 @@ def test_norm_ffn_validation_codes():
                      None) == 2                                                     # misaligned dx
     bad = vtb.make_ffn_cfg(8, 64, 0)
     assert L.ffn_bwd(ctypes.byref(bad), ctypes.byref(sv), out[0], out[1], out[2], out[3], out[3] + 0x800000, need, None) == 1
+
+
+def test_attn_block_validation_codes():
+    L = vtb.lib()
+    cfg = vtb.make_block_cfg(2, 16, 2, 8, 0.35)
+    need = vtb.attn_block_bwd_workspace_size(cfg)
+    assert need > 0
+    sv = vtb.AttnBlockSaved(A0, A1, A2, A3, A4, A5, A6)
+    out = [WS + 0x1000000 * i for i in range(1, 5)]
+    ok = lambda c=cfg, s=sv, dx2=out[0], dx=out[1], ws=out[3] + 0x800000, wsb=need: L.attn_block_bwd(
+        ctypes.byref(c), None if s is None else ctypes.byref(s), dx2, dx, out[2], out[3], ws, wsb, None)
+    assert ok(wsb=64) == 4                         # workspace too small
+    assert ok(dx=A3) == 3                          # dx overlaps qkv
+    assert ok(s=None) == 1
+    assert ok(dx=out[1] + 8) == 2                  # misaligned dx
+    bad = vtb.make_block_cfg(2, 16, 0, 8, 0.35)
+    assert ok(c=bad) == 1

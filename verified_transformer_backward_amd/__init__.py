@@ -29,6 +29,7 @@ EXPORTS = (
     "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd", "relu2_mul_bwd",
     "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
+    "attn_block_bwd_workspace_size", "attn_block_bwd",
 )
 
 
@@ -64,6 +65,18 @@ class LayerSaved(ctypes.Structure):
 
 class FfnBwdCfg(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("C", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class AttnBlockCfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+
+
+BLOCK_SAVED = ("ln_y", "ln_sig", "w_qkv", "qkv", "P", "ctx", "w_o")
+
+
+class AttnBlockSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_SAVED]
 
 
 FFN_SAVED = ("x", "gamma1", "xn", "w_gu", "gu", "gamma2", "hn", "w_down")
@@ -105,6 +118,9 @@ def lib() -> ctypes.CDLL:
         "layer_bwd": (ctypes.c_int, [ctypes.POINTER(LayerBwdCfg), ctypes.POINTER(LayerSaved), P, P, P, P, P, P, SZ, P]),
         "ffn_bwd_workspace_size": (SZ, [ctypes.POINTER(FfnBwdCfg)]),
         "ffn_bwd": (ctypes.c_int, [ctypes.POINTER(FfnBwdCfg), ctypes.POINTER(FfnSaved), P, P, P, P, P, SZ, P]),
+        "attn_block_bwd_workspace_size": (SZ, [ctypes.POINTER(AttnBlockCfg)]),
+        "attn_block_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBlockCfg), ctypes.POINTER(AttnBlockSaved), P, P, P, P, P, SZ,
+                                          P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -380,3 +396,39 @@ def ffn_bwd(saved: dict, dout, eps: float = 1e-6, dx=None, dw_gu=None, dw_down=N
     _check(lib().ffn_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dout), _ptr(dx), _ptr(dw_gu), _ptr(dw_down),
                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)), "ffn_bwd")
     return dx, dw_gu, dw_down
+
+
+def make_block_cfg(B, T, H, D, scale, causal=True) -> AttnBlockCfg:
+    c = AttnBlockCfg()
+    c.B, c.T, c.H, c.D, c.scale, c.causal = int(B), int(T), int(H), int(D), float(scale), int(bool(causal))
+    return c
+
+
+def attn_block_bwd_workspace_size(cfg: AttnBlockCfg) -> int:
+    return int(lib().attn_block_bwd_workspace_size(ctypes.byref(cfg)))
+
+
+def attn_block_bwd(saved: dict, dx2, B: int, H: int, scale: float, causal: bool = True, dx=None, dw_qkv=None,
+                   dw_o=None, workspace=None, stream=None):
+    """One attention block's backward over its saved tensors (ln_y, ln_sig, w_qkv, qkv, P,
+    ctx, w_o; fp32 contiguous); dx2 is [B T, C]. Returns (dx, dw_qkv, dw_o)."""
+    for n in BLOCK_SAVED:
+        t = saved[n]
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"saved[{n!r}] must be contiguous float32")
+    if dx2.dtype != torch.float32 or not dx2.is_contiguous():
+        raise TypeError("dx2 must be contiguous float32")
+    BT, C = dx2.shape
+    if BT % B or C % H:
+        raise ValueError("dx2 rows must be B * T and its width H * D")
+    cfg = make_block_cfg(B, BT // B, H, C // H, scale, causal)
+    sv = AttnBlockSaved(*[saved[n].data_ptr() for n in BLOCK_SAVED])
+    dx = torch.empty_like(dx2) if dx is None else dx
+    dw_qkv = torch.empty_like(saved["w_qkv"]) if dw_qkv is None else dw_qkv
+    dw_o = torch.empty_like(saved["w_o"]) if dw_o is None else dw_o
+    if workspace is None:
+        workspace = _workspace(attn_block_bwd_workspace_size(cfg), dx2.device)
+    _check(lib().attn_block_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dx2), _ptr(dx), _ptr(dw_qkv), _ptr(dw_o),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "attn_block_bwd")
+    return dx, dw_qkv, dw_o

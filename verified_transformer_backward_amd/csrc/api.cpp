@@ -397,7 +397,7 @@ int layernorm_bwd(int32_t dtype, const void* dy, const void* y, const float* sig
   const Span o = span_of(dx, bytes);
   if (overlap(o, span_of(dy, bytes)) || overlap(o, span_of(y, bytes)) || overlap(o, span_of(sig, (size_t)rows * 4)))
     return fail(VTB_ERR_ALIAS, "dx overlaps an input");
-  return hip_status(vtb::launch_layernorm_bwd(dtype == VTB_BF16, dy, y, sig, dx, rows, n,
+  return hip_status(vtb::launch_layernorm_bwd(dtype == VTB_BF16, dy, y, sig, nullptr, dx, rows, n,
                                               reinterpret_cast<hipStream_t>(stream)),
                     "layernorm_bwd");
 }
@@ -571,6 +571,89 @@ int ffn_bwd(const ffn_bwd_cfg* c, const ffn_saved* sv, const float* dout, float*
   if (rc) return rc;
   // 4. ffnNorm backward plus the residual: dx = dout + RMSNormBackward(x, gamma1, dxn)
   return hip_status(vtb::launch_rmsnorm_res_bwd(sv->x, sv->gamma1, dxn, dout, dx, T, C, c->eps, s), "ffn norm/residual");
+}
+
+
+size_t attn_block_bwd_workspace_size(const attn_block_cfg* c) {
+  if (!c || c->B < 1 || c->T < 1 || c->H < 1 || c->D < 1) return 0;
+  const size_t BT = (size_t)c->B * c->T, C = (size_t)c->H * c->D, T = c->T;
+  const int bt = c->B * c->T, ci = c->H * c->D;
+  // dctx [BT, C], dS [H, T, T], dqkv [BT, 3C], dln [BT, C], dX partials of either split product
+  const size_t parts = std::max((size_t)vtb::linear_bwd_splits(bt, ci, ci), (size_t)vtb::linear_bwd_splits(bt, ci, 3 * ci)) *
+                       BT * C;
+  return align256(BT * C * 4) * 2 + align256((size_t)c->H * T * T * 4) + align256(BT * 3 * C * 4) + align256(parts * 4);
+}
+
+int attn_block_bwd(const attn_block_cfg* c, const attn_block_saved* sv, const float* dx2, float* dx, float* dw_qkv,
+                   float* dw_o, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!c || !sv) return fail(VTB_ERR_ARG, "cfg and saved must be non-NULL");
+  if (c->B < 1 || c->T < 1 || c->H < 1 || c->D < 1)
+    return fail(VTB_ERR_ARG, "B=%d T=%d H=%d D=%d must be >= 1", c->B, c->T, c->H, c->D);
+  if (!std::isfinite(c->scale)) return fail(VTB_ERR_ARG, "scale is not finite");
+  if (c->causal != 0 && c->causal != 1) return fail(VTB_ERR_ARG, "causal must be 0 or 1");
+  const int64_t BT = (int64_t)c->B * c->T, C = (int64_t)c->H * c->D, T = c->T;
+  if (BT * 3 * C > ((int64_t)1 << 31) || C * 3 * C > ((int64_t)1 << 31) || (int64_t)c->B * c->H * T * T > ((int64_t)1 << 31))
+    return fail(VTB_ERR_UNSUPPORTED, "a tensor exceeds 2^31 elements");
+  const float* in_ptrs[8] = {sv->ln_y, sv->ln_sig, sv->w_qkv, sv->qkv, sv->P, sv->ctx, sv->w_o, dx2};
+  for (const float* ptr : in_ptrs)
+    if (!ptr) return fail(VTB_ERR_ARG, "a saved tensor or dx2 is NULL");
+  if (!dx || !dw_qkv || !dw_o) return fail(VTB_ERR_ARG, "outputs must be non-NULL");
+  for (const float* ptr : in_ptrs)
+    if (!aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (!aligned16(dx) || !aligned16(dw_qkv) || !aligned16(dw_o) || !aligned16(workspace))
+    return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const size_t in_bytes[8] = {(size_t)(BT * C * 4), (size_t)(BT * 4), (size_t)(C * 3 * C * 4), (size_t)(BT * 3 * C * 4),
+                              (size_t)((int64_t)c->B * c->H * T * T * 4), (size_t)(BT * C * 4), (size_t)(C * C * 4),
+                              (size_t)(BT * C * 4)};
+  Span ins[8];
+  for (int i = 0; i < 8; ++i) ins[i] = span_of(in_ptrs[i], in_bytes[i]);
+  const Span sdx = span_of(dx, BT * C * 4), sq = span_of(dw_qkv, C * 3 * C * 4), so = span_of(dw_o, C * C * 4);
+  for (int i = 0; i < 8; ++i) {
+    if (i != 7 && overlap(sdx, ins[i])) return fail(VTB_ERR_ALIAS, "dx overlaps saved tensor %d", i);
+    if (overlap(sq, ins[i]) || overlap(so, ins[i])) return fail(VTB_ERR_ALIAS, "a weight gradient overlaps input %d", i);
+  }
+  if (dx != dx2 && overlap(sdx, ins[7])) return fail(VTB_ERR_ALIAS, "dx partially overlaps dx2");
+  if (overlap(sdx, sq) || overlap(sdx, so) || overlap(sq, so)) return fail(VTB_ERR_ALIAS, "outputs overlap");
+  const size_t need = attn_block_bwd_workspace_size(c);
+  if (!workspace || workspace_bytes < need)
+    return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+  const Span sws = span_of(workspace, need);
+  for (int i = 0; i < 8; ++i)
+    if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps input %d", i);
+  if (overlap(sws, sdx) || overlap(sws, sq) || overlap(sws, so)) return fail(VTB_ERR_ALIAS, "workspace overlaps an output");
+
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int bt = (int)BT, ci = (int)C, H = c->H, D = c->D, Ti = c->T;
+  char* base = reinterpret_cast<char*>(workspace);
+  float* dctx = reinterpret_cast<float*>(base);
+  float* dln = reinterpret_cast<float*>(base + align256(BT * C * 4));
+  float* ds = reinterpret_cast<float*>(base + 2 * align256(BT * C * 4));
+  float* dqkv = reinterpret_cast<float*>(base + 2 * align256(BT * C * 4) + align256((size_t)H * T * T * 4));
+  float* part = reinterpret_cast<float*>(base + 2 * align256(BT * C * 4) + align256((size_t)H * T * T * 4) +
+                                         align256(BT * 3 * C * 4));
+
+  // 1. output projection: dctx = dx2 Wo^T, gWo = ctx^T dx2
+  int rc = hip_status(vtb::launch_linear_bwd_split(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, s), "block Wo");
+  if (rc) return rc;
+  // 2. attention backward with the saved softmax, one sequence at a time (dS reused),
+  //    gradients written into the q | k | v thirds of dqkv
+  for (int b = 0; b < c->B; ++b) {
+    const int64_t r3 = (int64_t)b * Ti * 3 * C, r1 = (int64_t)b * Ti * C;
+    const float* q = sv->qkv + r3;
+    float* dq = dqkv + r3;
+    rc = hip_status(vtb::launch_attn_saved_p_bwd_ld(q, q + C, q + 2 * C, dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq,
+                                                    dq + C, dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal,
+                                                    s),
+                    "block attention");
+    if (rc) return rc;
+  }
+  // 3. QKV projection as one product: dln = dqkv Wqkv^T, gWqkv = ln.y^T dqkv
+  rc = hip_status(vtb::launch_linear_bwd_split(sv->ln_y, sv->w_qkv, dqkv, dln, dw_qkv, bt, ci, 3 * ci, part, s),
+                  "block Wqkv");
+  if (rc) return rc;
+  // 4. LayerNorm backward plus the residual: dx = dx2 + lnBwd(dln, ln.y, sigma)
+  return hip_status(vtb::launch_layernorm_bwd(0, dln, sv->ln_y, sv->ln_sig, dx2, dx, bt, ci, s), "block layernorm");
 }
 
 }  // extern "C"

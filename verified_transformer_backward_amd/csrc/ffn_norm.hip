@@ -51,9 +51,11 @@ __device__ __forceinline__ float2 block_sum2_256(float a, float b) {
 // One 256-thread block per row; each thread holds NV 16-byte vectors of dy and y. Loads of
 // vectors past the row end are clamped to the row's last vector and masked out of the
 // sums and stores, so every load is issued before the reduction.
+// With dres (may be null) the residual is added: dx = dres + lnBwd(...); dx == dres is
+// allowed, each element of dres being read before the same thread writes it.
 template <typename E, int NV>
 __global__ __launch_bounds__(256) void layernorm_bwd_vec_kernel(const E* __restrict__ dy, const E* __restrict__ y,
-                                                                const float* __restrict__ sig, E* __restrict__ dx,
+                                                                const float* __restrict__ sig, const E* dres, E* dx,
                                                                 int n) {
   using V = typename Vec16<E>::type;
   constexpr int W = Vec16<E>::n;
@@ -62,12 +64,14 @@ __global__ __launch_bounds__(256) void layernorm_bwd_vec_kernel(const E* __restr
   const V* dyr = reinterpret_cast<const V*>(dy + row * n);
   const V* yr = reinterpret_cast<const V*>(y + row * n);
   V* dxr = reinterpret_cast<V*>(dx + row * n);
-  V a[NV], b[NV];
+  const V* rr = reinterpret_cast<const V*>(dres + row * n);
+  V a[NV], b[NV], c[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
     const int u = min((int)threadIdx.x + 256 * e, nvec - 1);
     a[e] = dyr[u];
     b[e] = yr[u];
+    if (dres) c[e] = rr[u];
   }
   const float s = sig[row];
   float sdy = 0.f, sdyy = 0.f;
@@ -91,7 +95,10 @@ __global__ __launch_bounds__(256) void layernorm_bwd_vec_kernel(const E* __restr
     if (u < nvec) {
       V o;
 #pragma unroll
-      for (int k = 0; k < W; ++k) o[k] = from_f32<E>((to_f32(a[e][k]) - mdy - to_f32(b[e][k]) * mdyy) * rs);
+      for (int k = 0; k < W; ++k) {
+        const float g = (to_f32(a[e][k]) - mdy - to_f32(b[e][k]) * mdyy) * rs;
+        o[k] = from_f32<E>(dres ? to_f32(c[e][k]) + g : g);
+      }
       __builtin_nontemporal_store(o, &dxr[u]);
     }
   }
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_vec_kernel(const E* __restr
 // thread per step.
 template <typename E>
 __global__ __launch_bounds__(256) void layernorm_bwd_any_kernel(const E* __restrict__ dy, const E* __restrict__ y,
-                                                                const float* __restrict__ sig, E* __restrict__ dx,
+                                                                const float* __restrict__ sig, const E* dres, E* dx,
                                                                 int n) {
   const int64_t row = blockIdx.x;
   const E* dyr = dy + row * n;
@@ -115,8 +122,10 @@ __global__ __launch_bounds__(256) void layernorm_bwd_any_kernel(const E* __restr
   const float2 tot = block_sum2_256(sdy, sdyy);
   const float mdy = tot.x / n, mdyy = tot.y / n;
   const float rs = 1.0f / sig[row];
-  for (int j = threadIdx.x; j < n; j += 256)
-    dx[row * n + j] = from_f32<E>((to_f32(dyr[j]) - mdy - to_f32(yr[j]) * mdyy) * rs);
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const float g = (to_f32(dyr[j]) - mdy - to_f32(yr[j]) * mdyy) * rs;
+    dx[row * n + j] = from_f32<E>(dres ? to_f32(dres[row * n + j]) + g : g);
+  }
 }
 
 // ---------------------------------------------------------------------- ReLU^2 x Mul backward
@@ -349,21 +358,22 @@ __global__ __launch_bounds__(256) void rmsnorm_res_bwd_any_kernel(const float* _
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <typename E>
-hipError_t layernorm_bwd_t(const E* dy, const E* y, const float* sig, E* dx, int rows, int n, hipStream_t s) {
+hipError_t layernorm_bwd_t(const E* dy, const E* y, const float* sig, const E* dres, E* dx, int rows, int n,
+                           hipStream_t s) {
   constexpr int W = Vec16<E>::n;
-  const bool vec = n % W == 0 && n <= 256 * W * 4 && al16(dy) && al16(y) && al16(dx);
+  const bool vec = n % W == 0 && n <= 256 * W * 4 && al16(dy) && al16(y) && al16(dx) && al16(dres);
   if (vec) {
     const int nv = (n / W + 255) / 256;
     if (nv <= 1)
-      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 1>), dim3(rows), dim3(256), 0, s, dy, y, sig, dx, n);
+      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 1>), dim3(rows), dim3(256), 0, s, dy, y, sig, dres, dx, n);
     else if (nv <= 2)
-      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 2>), dim3(rows), dim3(256), 0, s, dy, y, sig, dx, n);
+      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 2>), dim3(rows), dim3(256), 0, s, dy, y, sig, dres, dx, n);
     else if (nv <= 3)
-      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 3>), dim3(rows), dim3(256), 0, s, dy, y, sig, dx, n);
+      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 3>), dim3(rows), dim3(256), 0, s, dy, y, sig, dres, dx, n);
     else
-      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 4>), dim3(rows), dim3(256), 0, s, dy, y, sig, dx, n);
+      hipLaunchKernelGGL((layernorm_bwd_vec_kernel<E, 4>), dim3(rows), dim3(256), 0, s, dy, y, sig, dres, dx, n);
   } else {
-    hipLaunchKernelGGL(layernorm_bwd_any_kernel<E>, dim3(rows), dim3(256), 0, s, dy, y, sig, dx, n);
+    hipLaunchKernelGGL(layernorm_bwd_any_kernel<E>, dim3(rows), dim3(256), 0, s, dy, y, sig, dres, dx, n);
   }
   return hipGetLastError();
 }
@@ -429,13 +439,13 @@ hipError_t launch_rmsnorm_res_bwd(const float* x, const float* gamma, const floa
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm_bwd(int bf16, const void* dy, const void* y, const float* sig, void* dx, int rows, int n,
-                                hipStream_t s) {
+hipError_t launch_layernorm_bwd(int bf16, const void* dy, const void* y, const float* sig, const void* dres, void* dx,
+                                int rows, int n, hipStream_t s) {
   if (bf16)
-    return layernorm_bwd_t(static_cast<const __bf16*>(dy), static_cast<const __bf16*>(y), sig, static_cast<__bf16*>(dx),
-                           rows, n, s);
-  return layernorm_bwd_t(static_cast<const float*>(dy), static_cast<const float*>(y), sig, static_cast<float*>(dx), rows,
-                         n, s);
+    return layernorm_bwd_t(static_cast<const __bf16*>(dy), static_cast<const __bf16*>(y), sig,
+                           static_cast<const __bf16*>(dres), static_cast<__bf16*>(dx), rows, n, s);
+  return layernorm_bwd_t(static_cast<const float*>(dy), static_cast<const float*>(y), sig, static_cast<const float*>(dres),
+                         static_cast<float*>(dx), rows, n, s);
 }
 
 hipError_t launch_relu2_mul_bwd(int bf16, const void* gate, const void* up, const void* dh, void* dgate, void* dup,

@@ -414,8 +414,14 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows_kernel(const float* __re
 hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
                                    float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld, float scale,
                                    int causal, hipStream_t s) {
-  if (T < 1 || H < 1 || D < 1 || ld < H * D) return hipErrorInvalidValue;
-  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld % 4 == 0;
+  return launch_attn_saved_p_bwd_ld(q, k, v, dout, P, ds, dq, dk, dv, T, H, D, ld, ld, ld, scale, causal, s);
+}
+
+hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const float* v, const float* dout, const float* P,
+                                      float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld_in,
+                                      int ld_do, int ld_out, float scale, int causal, hipStream_t s) {
+  if (T < 1 || H < 1 || D < 1 || ld_in < H * D || ld_do < H * D || ld_out < H * D) return hipErrorInvalidValue;
+  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld_in % 4 == 0 && ld_do % 4 == 0 && ld_out % 4 == 0;
   auto base = [&](GemmDesc& g) {
     g = GemmDesc{};
     g.nsplit = 1;
@@ -427,8 +433,8 @@ hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* 
   // dP = dO V^T per head, on the (query, key) tiles that hold a visible pair
   GemmDesc gp;
   base(gp);
-  gp.A = dout; gp.am = ld; gp.ak = 1; gp.a_kc = 1; gp.a_b = D;
-  gp.B = v; gp.bk = 1; gp.bn = ld; gp.b_kc = 1; gp.b_b = D;
+  gp.A = dout; gp.am = ld_do; gp.ak = 1; gp.a_kc = 1; gp.a_b = D;
+  gp.B = v; gp.bk = 1; gp.bn = ld_in; gp.b_kc = 1; gp.b_b = D;
   gp.C = ds; gp.ldc = T; gp.c_b = (int64_t)T * T;
   gp.M = T; gp.N = T; gp.K = D; gp.kchunk = D;
   gp.tri = causal ? TRI_SCORES : TRI_NONE;
@@ -441,21 +447,22 @@ hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* 
   GemmDesc gq, gk, gv;
   base(gq);
   gq.A = ds; gq.am = T; gq.ak = 1; gq.a_kc = 1; gq.a_b = (int64_t)T * T;
-  gq.B = k; gq.bk = ld; gq.bn = 1; gq.b_kc = 0; gq.b_b = D;
-  gq.C = dq; gq.ldc = ld; gq.c_b = D;
+  gq.B = k; gq.bk = ld_in; gq.bn = 1; gq.b_kc = 0; gq.b_b = D;
+  gq.C = dq; gq.ldc = ld_out; gq.c_b = D;
   gq.M = T; gq.N = D; gq.K = T; gq.kchunk = T;
   gq.alpha = scale;
   gq.tri = causal ? TRI_KLE : TRI_NONE;
   base(gk);
   gk.A = ds; gk.am = 1; gk.ak = T; gk.a_kc = 0; gk.a_b = (int64_t)T * T;
-  gk.B = q; gk.bk = ld; gk.bn = 1; gk.b_kc = 0; gk.b_b = D;
-  gk.C = dk; gk.ldc = ld; gk.c_b = D;
+  gk.B = q; gk.bk = ld_in; gk.bn = 1; gk.b_kc = 0; gk.b_b = D;
+  gk.C = dk; gk.ldc = ld_out; gk.c_b = D;
   gk.M = T; gk.N = D; gk.K = T; gk.kchunk = T;
   gk.alpha = scale;
   gk.tri = causal ? TRI_KGE : TRI_NONE;
   gv = gk;
   gv.A = P;
   gv.B = dout;
+  gv.bk = ld_do;
   gv.C = dv;
   gv.alpha = 1.f;
   const int t0 = tiles_of(gq), t1 = tiles_of(gk), t2 = tiles_of(gv);

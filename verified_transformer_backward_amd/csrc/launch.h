@@ -91,9 +91,10 @@ hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const fl
                                        float eps, hipStream_t s);
 
 // LayerNorm (no affine) backward from the forward's y and sigma, rows of n values, fp32 or
-// bf16 storage (bf16 != 0) with fp32 arithmetic; sigma is fp32.
-hipError_t launch_layernorm_bwd(int bf16, const void* dy, const void* y, const float* sig, void* dx, int rows, int n,
-                                hipStream_t s);
+// bf16 storage (bf16 != 0) with fp32 arithmetic; sigma is fp32. dres (may be null) is a
+// residual gradient added to the result; dx == dres is allowed.
+hipError_t launch_layernorm_bwd(int bf16, const void* dy, const void* y, const float* sig, const void* dres, void* dx,
+                                int rows, int n, hipStream_t s);
 // ReLU^2 x Mul backward over n elements, fp32 or bf16 storage.
 hipError_t launch_relu2_mul_bwd(int bf16, const void* gate, const void* up, const void* dh, void* dgate, void* dup,
                                 int64_t n, hipStream_t s);
@@ -123,5 +124,10 @@ hipError_t launch_linear_bwd_split(const float* x, const float* w, const float* 
 hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
                                    float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld, float scale,
                                    int causal, hipStream_t s);
+// The same with separate row strides: ld_in for q, k, v; ld_do for dout; ld_out for dq,
+// dk, dv (q, k, v and their gradients can then sit in one [T, 3C] row).
+hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const float* v, const float* dout, const float* P,
+                                      float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld_in,
+                                      int ld_do, int ld_out, float scale, int causal, hipStream_t s);
 
 }  // namespace vtb
