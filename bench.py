@@ -153,7 +153,7 @@ def graph_ms(torch, hip, fn, reps):
 
 
 EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd",
-               "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd")
+               "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
 def extra_workloads(torch, vtb, hip, only=None):
@@ -317,6 +317,42 @@ def extra_workloads(torch, vtb, hip, only=None):
                                        "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
                                        "algorithmic_flops": fl}}
         del saved, x, xn, gu, hn, wgu, wd, dx, dwgu, dwd, fws
+
+    if want("attn_block_bwd"):
+        # one transformer attention block's backward (LayerNorm, QKV and output projections,
+        # causal attention with the saved softmax), T256 20 x 128 fp32; saved activations
+        # from a torch fp32 forward (setup only)
+        Tb, Hb, db = 256, 20, 128
+        Cb = Hb * db
+        sc = 1.0 / np.sqrt(db)
+        p = synth.block_inputs(1, Tb, Hb, db)
+        xin, wqkv, wo, dx2 = (up(p[n]) for n in ("xin", "w_qkv", "w_o", "dx2"))
+        mu = xin.mean(1, keepdim=True)
+        sig = torch.sqrt(((xin - mu) ** 2).mean(1) + 1e-5).contiguous()
+        ln_y = ((xin - mu) / sig[:, None]).contiguous()
+        qkv = (ln_y @ wqkv).contiguous()
+        hsplit = lambda z: z.reshape(Tb, Hb, db).permute(1, 0, 2).contiguous()
+        q, k, v = hsplit(qkv[:, :Cb]), hsplit(qkv[:, Cb:2 * Cb]), hsplit(qkv[:, 2 * Cb:])
+        mask = torch.tril(torch.ones(Tb, Tb, dtype=torch.bool, device=dev))
+        S = torch.matmul(q, k.transpose(1, 2).contiguous()) * sc
+        P = torch.softmax(S.masked_fill(~mask, float("-inf")), -1).contiguous()
+        ctx = torch.matmul(P, v).permute(1, 0, 2).reshape(Tb, Cb).contiguous()
+        saved = {"ln_y": ln_y, "ln_sig": sig, "w_qkv": wqkv, "qkv": qkv, "P": P, "ctx": ctx, "w_o": wo}
+        dx, dwq, dwo = torch.empty_like(dx2), torch.empty_like(wqkv), torch.empty_like(wo)
+        bws = torch.empty(vtb.attn_block_bwd_workspace_size(vtb.make_block_cfg(1, Tb, Hb, db, sc)), dtype=torch.uint8,
+                          device=dev)
+        f = lambda: vtb.attn_block_bwd(saved, dx2, 1, Hb, sc, True, dx=dx, dw_qkv=dwq, dw_o=dwo, workspace=bws,
+                                       stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 10)
+        pairs = Hb * Tb * (Tb + 1) // 2
+        fl = 4 * Tb * Cb * Cb + 4 * Tb * Cb * 3 * Cb + 8 * db * pairs   # Wo, Wqkv products; 4 attention contractions
+        out["attn_block_bwd"] = {"workload": "attention block backward (LayerNorm, QKV/output projections, saved-softmax "
+                                             "causal attention), T256 20 x 128 fp32",
+                                 "ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                                 "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
+                                              "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                                              "algorithmic_flops": fl}}
+        del saved, xin, wqkv, wo, dx2, ln_y, qkv, P, ctx, dx, dwq, dwo, bws
 
     if want("layer_chain"):
         # 30-layer chain: T256, hidden 2560 = 20 x 128, fp32, saved softmax P per layer

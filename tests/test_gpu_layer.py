@@ -205,3 +205,46 @@ def test_layer_chain_30_layers_full_size():
                 say(f"layer{l}.{n} rel_err={e:.2e}")
     e = assert_close("chain.g0", host(g), gr, TOL["f32"])
     say(f"chain.g0 rel_err={e:.2e}")
+
+
+def test_layer_bwd_graph_replays_match_eager():
+    # a graph captured over a two-layer chain (dh_in written over dh_out) must replay, again
+    # and again with eager work in between, to the eager results bit for bit
+    need_gpu()
+    T, H, d = 64, 2, 64
+    say("layer_bwd graph capture: two layers T64 H2 d64, three replays")
+    sc = 1.0 / np.sqrt(d)
+    sds = [_saved_to_dev(_layer_case(l, T, H, d)[0]) for l in range(2)]
+    g0 = dev(synth.layer_upstream_grad(T=T, H=H, d=d))
+    cfg = vtb.make_layer_cfg(T, H, d, sc)
+    ws = torch.empty(vtb.layer_bwd_workspace_size(cfg), dtype=torch.uint8, device="cuda:0")
+    g = torch.empty_like(g0)
+    outs = [(torch.empty_like(sds[l]["w"]), torch.empty_like(sds[l]["k"]), torch.empty_like(sds[l]["v"])) for l in range(2)]
+
+    def chain():
+        g.copy_(g0)
+        for l in (1, 0):
+            dw, dk, dv = outs[l]
+            vtb.layer_bwd(sds[l], g, sc, dh_in=g, dw=dw, dk=dk, dv=dv, workspace=ws, stream=torch.cuda.current_stream())
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [g.clone()] + [t.clone() for o in outs for t in o]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        chain()
+    for rep in range(3):
+        g.zero_()
+        for o in outs:
+            for t in o:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [g] + [t for o in outs for t in o]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
