@@ -156,6 +156,19 @@ EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rms
                "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
+def copy_bandwidth(torch, hip):
+    """A plain 1 GiB device-to-device copy (torch copy_: read 1 GiB, write 1 GiB), graph-replayed,
+    for context beside the spec peak. Not a ceiling (the library's streaming kernels run faster)
+    and never a roofline denominator."""
+    src = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms = graph_ms(torch, hip, lambda: dst.copy_(src), 5)
+    byts = 2 * src.numel() * 4
+    del src, dst
+    return {"what": "1 GiB device copy (torch copy_), read + write", "ms": round(ms, 4),
+            "gbps": round(byts / (ms * 1e-3) / 1e9, 1), "frac_of_spec": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def extra_workloads(torch, vtb, hip, only=None):
     """The other rows of the hot path at their workload sizes, each against its roofline.
     Inputs are seeded synthetic tensors; the layer chain's saved activations come from a
@@ -426,7 +439,13 @@ def cpu_baseline(x, seconds):
         dt += time.perf_counter() - t0
         done += 1
     flops = 10 * d * done * T * (T + 1) // 2
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "cpu_model": cpu,
             "sample": f"{done} single-head backwards cycling over the {len(heads)} (b,h) heads of "
                       f"B{B} H{H} T{T} d{d}, float64 numpy, {dt:.1f} s timed"}
 
@@ -598,6 +617,7 @@ def main():
     }
     if not args.no_extra:
         out["other_workloads"] = extra_workloads(torch, vtb, hip)
+        out["measured_hbm_copy"] = copy_bandwidth(torch, hip)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
