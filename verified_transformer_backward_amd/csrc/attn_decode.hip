@@ -307,12 +307,15 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
       EO* dkp = reinterpret_cast<EO*>(p.dk) + (int64_t)b * p.sdk[0] + (int64_t)j * p.sdk[1] + (int64_t)kvh * p.sdk[2] + 4 * c4;
       EO* dvp = reinterpret_cast<EO*>(p.dv) + (int64_t)b * p.sdv[0] + (int64_t)j * p.sdv[1] + (int64_t)kvh * p.sdv[2] + 4 * c4;
       const float sc = p.scale;
+      // dK and dV are written once and never read here: nontemporal stores
       if constexpr (std::is_same<EO, float>::value) {
-        *reinterpret_cast<float4*>(dkp) = make_float4(ak.x * sc, ak.y * sc, ak.z * sc, ak.w * sc);
-        *reinterpret_cast<float4*>(dvp) = av;
+        __builtin_nontemporal_store(f32x4{ak.x * sc, ak.y * sc, ak.z * sc, ak.w * sc}, reinterpret_cast<f32x4*>(dkp));
+        __builtin_nontemporal_store(f32x4{av.x, av.y, av.z, av.w}, reinterpret_cast<f32x4*>(dvp));
       } else {
-        *reinterpret_cast<bf16x4*>(dkp) = bf16x4{(__bf16)(ak.x * sc), (__bf16)(ak.y * sc), (__bf16)(ak.z * sc), (__bf16)(ak.w * sc)};
-        *reinterpret_cast<bf16x4*>(dvp) = bf16x4{(__bf16)av.x, (__bf16)av.y, (__bf16)av.z, (__bf16)av.w};
+        __builtin_nontemporal_store(bf16x4{(__bf16)(ak.x * sc), (__bf16)(ak.y * sc), (__bf16)(ak.z * sc), (__bf16)(ak.w * sc)},
+                                    reinterpret_cast<bf16x4*>(dkp));
+        __builtin_nontemporal_store(bf16x4{(__bf16)av.x, (__bf16)av.y, (__bf16)av.z, (__bf16)av.w},
+                                    reinterpret_cast<bf16x4*>(dvp));
       }
     }
   }
