@@ -409,6 +409,45 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows_kernel(const float* __re
   for (int j = lane; j < T; j += 64) dr[j] = j <= lim ? pr[j] * (dr[j] - acc) : 0.f;
 }
 
+// The same with float4 moves for rows of T = 4 T4 <= 256 NV values (16-byte aligned): lane l
+// holds float4s l, l + 64, ... of P and dP in registers between the sum and the store, and
+// float4s wholly past the row's last visible key are neither read nor summed.
+template <int NV>
+__global__ __launch_bounds__(256) void softmax_bwd_rows_vec_kernel(const f32x4* __restrict__ P, f32x4* __restrict__ ds,
+                                                                   int rows, int T, int causal) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int i = r % T, lim = causal ? i : T - 1, T4 = T / 4;
+  const f32x4* pr = P + (int64_t)r * T4;
+  f32x4* dr = ds + (int64_t)r * T4;
+  f32x4 pv[NV], dv[NV];
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int c = lane + 64 * e, j = 4 * c;
+    pv[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[e] = pv[e];
+    if (c < T4 && j <= lim) {
+      pv[e] = pr[c];
+      dv[e] = dr[c];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc = j + k <= lim ? fmaf(pv[e][k], dv[e][k], acc) : acc;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int c = lane + 64 * e, j = 4 * c;
+    if (c < T4) {
+      f32x4 out;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[k] = j + k <= lim ? pv[e][k] * (dv[e][k] - acc) : 0.f;
+      dr[c] = out;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
@@ -441,7 +480,16 @@ hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const floa
   const int tp = tiles_of(gp);
   hipLaunchKernelGGL(gemm_f32_kernel, dim3(tp), dim3(256), 0, s, gp, gp, gp, tp, 0);
   const int rows = H * T;
-  hipLaunchKernelGGL(softmax_bwd_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, P, ds, rows, T, causal);
+  const bool rv = T % 4 == 0 && T <= 1024 && ((uintptr_t)P | (uintptr_t)ds) % 16 == 0;
+  const int nv = (T / 4 + 63) / 64;
+  if (rv && nv <= 1)
+    hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<1>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       reinterpret_cast<const f32x4*>(P), reinterpret_cast<f32x4*>(ds), rows, T, causal);
+  else if (rv)
+    hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<4>, dim3((rows + 3) / 4), dim3(256), 0, s,
+                       reinterpret_cast<const f32x4*>(P), reinterpret_cast<f32x4*>(ds), rows, T, causal);
+  else
+    hipLaunchKernelGGL(softmax_bwd_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, P, ds, rows, T, causal);
   // dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO per head, contraction limited to the
   // visible keys (dQ) or queries (dK, dV)
   GemmDesc gq, gk, gv;
