@@ -350,6 +350,14 @@ def layer_bwd(saved: dict, dh_out, scale: float, eps: float = 1e-6, rope_base: f
         t = saved[n]
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError(f"saved[{n!r}] must be contiguous float32")
+    C = H * D
+    want = {"x": (T, C), "gamma": (C,), "w": (C, C), "o": (T, C), "q": (T, H, D), "k": (T, H, D), "v": (T, H, D),
+            "P": (H, T, T)}
+    for n, shp in want.items():
+        if tuple(saved[n].shape) != shp:
+            raise ValueError(f"saved[{n!r}] has shape {tuple(saved[n].shape)}, expected {shp}")
+    if tuple(dh_out.shape) != (T, C):
+        raise ValueError(f"dh_out must be {(T, C)}")
     cfg = make_layer_cfg(T, H, D, scale, eps, rope_base, rope_layout, causal)
     sv = LayerSaved(*[saved[n].data_ptr() for n in ("x", "gamma", "w", "o", "q", "k", "v", "P")])
     dev = dh_out.device
@@ -385,6 +393,13 @@ def ffn_bwd(saved: dict, dout, eps: float = 1e-6, dx=None, dw_gu=None, dw_down=N
         raise TypeError("dout must be contiguous float32")
     T, C = saved["x"].shape
     F = saved["w_down"].shape[0]
+    want = {"x": (T, C), "gamma1": (C,), "xn": (T, C), "w_gu": (C, 2 * F), "gu": (T, 2 * F), "gamma2": (F,),
+            "hn": (T, F), "w_down": (F, C)}
+    for n, shp in want.items():
+        if tuple(saved[n].shape) != shp:
+            raise ValueError(f"saved[{n!r}] has shape {tuple(saved[n].shape)}, expected {shp}")
+    if tuple(dout.shape) != (T, C):
+        raise ValueError(f"dout must be {(T, C)}")
     cfg = make_ffn_cfg(T, C, F, eps)
     sv = FfnSaved(*[saved[n].data_ptr() for n in FFN_SAVED])
     dx = torch.empty_like(dout) if dx is None else dx
@@ -421,7 +436,13 @@ def attn_block_bwd(saved: dict, dx2, B: int, H: int, scale: float, causal: bool 
     BT, C = dx2.shape
     if BT % B or C % H:
         raise ValueError("dx2 rows must be B * T and its width H * D")
-    cfg = make_block_cfg(B, BT // B, H, C // H, scale, causal)
+    T = BT // B
+    want = {"ln_y": (BT, C), "ln_sig": (BT,), "w_qkv": (C, 3 * C), "qkv": (BT, 3 * C), "P": (B * H, T, T),
+            "ctx": (BT, C), "w_o": (C, C)}
+    for n, shp in want.items():
+        if tuple(saved[n].shape) != shp:
+            raise ValueError(f"saved[{n!r}] has shape {tuple(saved[n].shape)}, expected {shp}")
+    cfg = make_block_cfg(B, T, H, C // H, scale, causal)
     sv = AttnBlockSaved(*[saved[n].data_ptr() for n in BLOCK_SAVED])
     dx = torch.empty_like(dx2) if dx is None else dx
     dw_qkv = torch.empty_like(saved["w_qkv"]) if dw_qkv is None else dw_qkv
