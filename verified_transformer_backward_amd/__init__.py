@@ -160,6 +160,15 @@ def _bthd_strides(t: torch.Tensor, name: str):
     return (t.stride(0), t.stride(1), t.stride(2))
 
 
+def _out(t, shape, name: str, device):
+    """A caller-given fp32 output, checked for shape, dtype and layout, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 {tuple(shape)}")
+    return t
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -361,10 +370,10 @@ def layer_bwd(saved: dict, dh_out, scale: float, eps: float = 1e-6, rope_base: f
     cfg = make_layer_cfg(T, H, D, scale, eps, rope_base, rope_layout, causal)
     sv = LayerSaved(*[saved[n].data_ptr() for n in ("x", "gamma", "w", "o", "q", "k", "v", "P")])
     dev = dh_out.device
-    dh_in = torch.empty_like(dh_out) if dh_in is None else dh_in
-    dw = torch.empty_like(saved["w"]) if dw is None else dw
-    dk = torch.empty_like(saved["k"]) if dk is None else dk
-    dv = torch.empty_like(saved["v"]) if dv is None else dv
+    dh_in = _out(dh_in, (T, C), "dh_in", dev)
+    dw = _out(dw, (C, C), "dw", dev)
+    dk = _out(dk, (T, H, D), "dk", dev)
+    dv = _out(dv, (T, H, D), "dv", dev)
     if workspace is None:
         workspace = _workspace(layer_bwd_workspace_size(cfg), dev)
     _check(lib().layer_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dh_out), _ptr(dh_in), _ptr(dw), _ptr(dk), _ptr(dv),
@@ -402,9 +411,9 @@ def ffn_bwd(saved: dict, dout, eps: float = 1e-6, dx=None, dw_gu=None, dw_down=N
         raise ValueError(f"dout must be {(T, C)}")
     cfg = make_ffn_cfg(T, C, F, eps)
     sv = FfnSaved(*[saved[n].data_ptr() for n in FFN_SAVED])
-    dx = torch.empty_like(dout) if dx is None else dx
-    dw_gu = torch.empty_like(saved["w_gu"]) if dw_gu is None else dw_gu
-    dw_down = torch.empty_like(saved["w_down"]) if dw_down is None else dw_down
+    dx = _out(dx, (T, C), "dx", dout.device)
+    dw_gu = _out(dw_gu, (C, 2 * F), "dw_gu", dout.device)
+    dw_down = _out(dw_down, (F, C), "dw_down", dout.device)
     need = ffn_bwd_workspace_size(cfg)
     if workspace is None:
         workspace = _workspace(need, dout.device)
@@ -444,9 +453,9 @@ def attn_block_bwd(saved: dict, dx2, B: int, H: int, scale: float, causal: bool 
             raise ValueError(f"saved[{n!r}] has shape {tuple(saved[n].shape)}, expected {shp}")
     cfg = make_block_cfg(B, T, H, C // H, scale, causal)
     sv = AttnBlockSaved(*[saved[n].data_ptr() for n in BLOCK_SAVED])
-    dx = torch.empty_like(dx2) if dx is None else dx
-    dw_qkv = torch.empty_like(saved["w_qkv"]) if dw_qkv is None else dw_qkv
-    dw_o = torch.empty_like(saved["w_o"]) if dw_o is None else dw_o
+    dx = _out(dx, (BT, C), "dx", dx2.device)
+    dw_qkv = _out(dw_qkv, (C, 3 * C), "dw_qkv", dx2.device)
+    dw_o = _out(dw_o, (C, C), "dw_o", dx2.device)
     if workspace is None:
         workspace = _workspace(attn_block_bwd_workspace_size(cfg), dx2.device)
     _check(lib().attn_block_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dx2), _ptr(dx), _ptr(dw_qkv), _ptr(dw_o),
