@@ -361,11 +361,15 @@ hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, fl
   return hipGetLastError();
 }
 
+#ifndef VTB_SPLITK_STEPS           // target k steps per dX chunk of the split contraction
+#define VTB_SPLITK_STEPS 24
+#endif
+
 int linear_bwd_splits(int T, int K, int N) {
   (void)T;
   (void)K;
   const int nk = (N + KT - 1) / KT;   // k steps of dX's contraction
-  const int want = std::max(1, std::min(8, nk / 16));
+  const int want = std::max(1, std::min(8, nk / VTB_SPLITK_STEPS));
   const int per = (nk + want - 1) / want;
   return (nk + per - 1) / per;        // every chunk non-empty
 }
