@@ -71,6 +71,19 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70
 // so LDS reads run ahead of the MFMAs that consume them.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Issue priority of the wave: raised over each run of MFMAs and lowered for the softmax
+// arithmetic between them, so that of the two waves sharing a SIMD the one with matrix
+// work ready issues it first and the other's vector work fills in around it.
+#ifndef VTB_MFMA_SETPRIO
+#define VTB_MFMA_SETPRIO 1
+#endif
+__device__ __forceinline__ void prio_mfma() {
+  if (VTB_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_valu() {
+  if (VTB_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 // Direct-to-LDS loads, issued through inline assembly. Each lane reads `bytes` bytes at
 // sbase + voff (sbase wave-uniform) and writes them to LDS at m0 + lane * bytes. Written
 // as assembly so that the compiler does not treat the asynchronous LDS write as aliasing
@@ -230,6 +243,7 @@ void dq_mfma_kernel(AttnParams p) {
         av[ks] = row8<LT>(sV, 16 * kt + lc, 32 * ks + 8 * lg);
       }
     };
+    prio_mfma();
     read_rows(0, fk[0], fv[0]);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -248,6 +262,7 @@ void dq_mfma_kernel(AttnParams p) {
       }
       fence();
     }
+    prio_valu();
     // K^T fragments of the first (dt, c) pairs are read under the softmax arithmetic.
     constexpr int NP = kNDT * 2, AHEAD = 4;
     bf16x8 kT[AHEAD + 1];
@@ -294,6 +309,7 @@ void dq_mfma_kernel(AttnParams p) {
           xb[kt >> 1][qt][4 * (kt & 1) + r] = xr;
         }
     fence();
+    prio_mfma();
     // A^T += K^T (P o dP)^T,  B^T += K^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
@@ -308,6 +324,7 @@ void dq_mfma_kernel(AttnParams p) {
       }
       fence();
     }
+    prio_valu();
   };
 
   // Block j sits in buffer j % 2. After the barrier every wave has finished block j - 1,
@@ -439,6 +456,7 @@ void fwd_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < kNKS; ++ks) ak[ks] = row8<LT>(sK, 16 * kt + lc, 32 * ks + 8 * lg);
     };
+    prio_mfma();
     read_rows(0, fk[0]);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -453,6 +471,7 @@ void fwd_mfma_kernel(AttnParams p) {
       }
       fence();
     }
+    prio_valu();
     // V^T fragments of the first (dt, c) pairs are read under the softmax arithmetic.
     constexpr int NP = kNDT * 2, AHEAD = 4;
     bf16x8 vT[AHEAD + 1];
@@ -513,6 +532,7 @@ void fwd_mfma_kernel(AttnParams p) {
       mrun[qt] = mn;
     }
     fence();
+    prio_mfma();
     // O^T += V^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
@@ -524,6 +544,7 @@ void fwd_mfma_kernel(AttnParams p) {
       for (int qt = 0; qt < kNT; ++qt) mma(acO[dt][qt], vT[pr % (AHEAD + 1)], pb[c][qt]);
       fence();
     }
+    prio_valu();
   };
 
   auto iteration = [&](int j, auto buf_c) {
@@ -654,6 +675,7 @@ void dkdv_mfma_kernel(AttnParams p) {
         ao[ks] = row8<LT>(sO, 16 * qt + lc, 32 * ks + 8 * lg);
       }
     };
+    prio_mfma();
     read_rows(0, fq[0], fo[0]);
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -672,6 +694,7 @@ void dkdv_mfma_kernel(AttnParams p) {
       }
       fence();
     }
+    prio_valu();
     // dO^T and Q^T fragments of the first (dt, c) pairs are read under the arithmetic.
     constexpr int NP = kNDT * 2, AHEAD = 3;
     bf16x8 oT[AHEAD + 1], qT[AHEAD + 1];
@@ -725,6 +748,7 @@ void dkdv_mfma_kernel(AttnParams p) {
         }
     }
     fence();
+    prio_mfma();
     // dV^T += dO^T P,  dK^T += Q^T dS over (dt, c) pairs (scale applied at the end)
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
@@ -739,6 +763,7 @@ void dkdv_mfma_kernel(AttnParams p) {
       }
       fence();
     }
+    prio_valu();
   };
 
   // Iteration it works on (head h, query block q0); (hs, q0s) is the iteration whose
