@@ -74,6 +74,14 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // Issue priority of the wave: raised over each run of MFMAs and lowered for the softmax
 // arithmetic between them, so that of the two waves sharing a SIMD the one with matrix
 // work ready issues it first and the other's vector work fills in around it.
+// Transposed operand fragments read ahead of their MFMAs in the (P o dP)K / PK (dq) and
+// dO^T P / Q^T dS (dk/dv) loops.
+#ifndef VTB_DQ_AHEAD
+#define VTB_DQ_AHEAD 4
+#endif
+#ifndef VTB_DKDV_AHEAD
+#define VTB_DKDV_AHEAD 3
+#endif
 #ifndef VTB_MFMA_SETPRIO
 #define VTB_MFMA_SETPRIO 1
 #endif
@@ -264,7 +272,7 @@ void dq_mfma_kernel(AttnParams p) {
     }
     prio_valu();
     // K^T fragments of the first (dt, c) pairs are read under the softmax arithmetic.
-    constexpr int NP = kNDT * 2, AHEAD = 4;
+    constexpr int NP = kNDT * 2, AHEAD = VTB_DQ_AHEAD;
     bf16x8 kT[AHEAD + 1];
     auto read_kT = [&](int pr) { return col8<LT>(sK, 32 * (pr & 1) + 4 * lg, 32 * (pr & 1) + 16 + 4 * lg, 16 * (pr >> 1)); };
 #pragma unroll
@@ -696,7 +704,7 @@ void dkdv_mfma_kernel(AttnParams p) {
     }
     prio_valu();
     // dO^T and Q^T fragments of the first (dt, c) pairs are read under the arithmetic.
-    constexpr int NP = kNDT * 2, AHEAD = 3;
+    constexpr int NP = kNDT * 2, AHEAD = VTB_DKDV_AHEAD;
     bf16x8 oT[AHEAD + 1], qT[AHEAD + 1];
     auto read_T = [&](int pr, bf16x8& o, bf16x8& q) {
       const int c = pr & 1, dt = pr >> 1;
