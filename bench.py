@@ -169,6 +169,23 @@ def copy_bandwidth(torch, hip):
             "gbps": round(byts / (ms * 1e-3) / 1e9, 1), "frac_of_spec": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def library_gemm_rates(torch, hip):
+    """Measured matrix-core reference: a square 8192^3 torch matmul (the vendor BLAS, contiguous
+    operands) in bf16 and in fp32, graph-replayed. Context beside the spec peaks, never a
+    roofline denominator."""
+    out = {}
+    for name, dt, reps in (("bf16", torch.bfloat16, 10), ("fp32", torch.float32, 2)):
+        n = 8192
+        g = torch.Generator(device="cuda:0").manual_seed(1)
+        a = torch.randn(n, n, generator=g, device="cuda:0").to(dt)
+        b = torch.randn(n, n, generator=g, device="cuda:0").to(dt)
+        c = torch.empty(n, n, device="cuda:0", dtype=dt)
+        ms = graph_ms(torch, hip, lambda: torch.mm(a, b, out=c), reps)
+        out[name] = {"what": f"torch.mm {n}^3 {name}", "ms": round(ms, 3), "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+        del a, b, c
+    return out
+
+
 def extra_workloads(torch, vtb, hip, only=None):
     """The other rows of the hot path at their workload sizes, each against its roofline.
     Inputs are seeded synthetic tensors; the layer chain's saved activations come from a
@@ -618,6 +635,7 @@ def main():
     if not args.no_extra:
         out["other_workloads"] = extra_workloads(torch, vtb, hip)
         out["measured_hbm_copy"] = copy_bandwidth(torch, hip)
+        out["measured_library_gemm"] = library_gemm_rates(torch, hip)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
