@@ -201,6 +201,11 @@ def extra_workloads(torch, vtb, hip, only=None):
     def want(name):
         return only is None or name in only
 
+    def hbm_line(name, what, ms, byts):
+        out[name] = {"workload": what, "ms": round(ms, 5), "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                     "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes": byts}}
+
     def up(a, dtype="f32"):
         if dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(synth.bf16_bits(a))).view(torch.bfloat16).to(dev)
@@ -289,12 +294,16 @@ def extra_workloads(torch, vtb, hip, only=None):
                               "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                               "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                            "algorithmic_bytes": byts}}
-        del dq_, xx, dh, dh_in, dy3, dx3
-
-    def hbm_line(name, what, ms, byts):
-        out[name] = {"workload": what, "ms": round(ms, 5), "value": round(byts / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                     "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "algorithmic_bytes": byts}}
+        # the same RoPE and RMSNorm backwards in bf16 storage (fp32 arithmetic, gamma fp32)
+        xb, db = xx.to(torch.bfloat16), dh.to(torch.bfloat16)
+        dy3b, dx3b, dxb = db.view(rows, H, d), torch.empty_like(db).view(rows, H, d), torch.empty_like(db)
+        f = lambda: vtb.rope_bwd(dy3b, dx=dx3b, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        hbm_line("rope_bwd_bf16", "RoPE backward, 7680 x 20 x 128 bf16", ms, 2 * rows * C * 2)
+        f = lambda: vtb.rmsnorm_bwd(xb, gam, db, dx=dxb, stream=torch.cuda.current_stream())
+        ms = graph_ms(torch, hip, f, 20)
+        hbm_line("rmsnorm_bwd_bf16", "RMSNorm backward, 7680 x 2560 bf16", ms, 3 * rows * C * 2 + C * 4)
+        del dq_, xx, dh, dh_in, dy3, dx3, xb, db, dy3b, dx3b, dxb
 
     if want("layernorm_bwd"):
         # LayerNorm (no affine) backward, 7680 x 2560: dy, y read, dx written, sigma per row

@@ -150,6 +150,15 @@ int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t
 int rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int32_t rows,
                 int32_t n, float eps, vtb_stream_t stream);
 
+/* The same two operations with the storage type as an argument: dtype VTB_F32 or VTB_BF16
+ * for dy, dx (RoPE) and x, dy, dx (RMSNorm), fp32 arithmetic, outputs rounded once (RNE
+ * for bf16); gamma stays fp32. Layouts, aliasing rules and errors as above. */
+int rope_bwd_ex(int32_t dtype, const void* dy, void* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim,
+                int64_t tok_stride, const int32_t* pos, int32_t pos0, double base, int32_t layout,
+                vtb_stream_t stream);
+int rmsnorm_bwd_ex(int32_t dtype, const void* x, const float* gamma, const void* dy, void* dx, int32_t rows,
+                   int32_t n, float eps, vtb_stream_t stream);
+
 /* Fused tail of one layer's backward (RoPE backward, RMSNorm backward, residual):
  *     dh_in = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq))
  * per token row of C = n_heads * head_dim values, positions pos0 + t. dq: [T, C] fp32

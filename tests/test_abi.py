@@ -145,3 +145,12 @@ def test_attn_block_validation_codes():
     assert ok(dx=out[1] + 8) == 2                  # misaligned dx
     bad = vtb.make_block_cfg(2, 16, 0, 8, 0.35)
     assert ok(c=bad) == 1
+
+
+def test_bf16_elementwise_entry_points_validate():
+    L = vtb.lib()
+    assert L.rope_bwd_ex(5, A0, A1, 4, 2, 8, 16, None, 0, 10000.0, 0, None) == 1        # dtype
+    assert L.rope_bwd_ex(1, A0, A0 + 8, 4, 2, 8, 16, None, 0, 10000.0, 0, None) == 3    # partial overlap
+    assert L.rope_bwd_ex(1, A0, A1, 0, 2, 8, 16, None, 0, 10000.0, 0, None) == 0        # no tokens
+    assert L.rmsnorm_bwd_ex(1, A0, A1, A2, A0, 4, 64, 1e-6, None) == 3                  # dx aliases x
+    assert L.rmsnorm_bwd_ex(9, A0, A1, A2, A3, 4, 64, 1e-6, None) == 1

@@ -248,3 +248,49 @@ def test_layer_bwd_graph_replays_match_eager():
         got = [g] + [t for o in outs for t in o]
         for i, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+
+
+# bf16 storage: (T, H, d, layout, token pad) on the 8-element vector kernel (rows of up to
+# 2048 vectors, both layouts) and on the per-pair kernel (head_dim not a multiple of 8, or
+# of 16 for the half-split layout, and rows wider than the vector kernel)
+@pytest.mark.parametrize("T,H,d,layout,pad", [(29, 20, 128, 0, 8), (29, 4, 64, 1, 16), (11, 3, 12, 0, 0),
+                                               (11, 3, 24, 1, 0), (5, 80, 128, 0, 0), (3, 160, 128, 1, 0)])
+def test_rope_bf16(T, H, d, layout, pad):
+    need_gpu()
+    say(f"rope bf16 T {T} H {H} d {d} layout {layout} token pad {pad}")
+    rng = np.random.default_rng(T * 1000 + d + layout)
+    full = synth.bf16_round(rng.standard_normal((T, H * d + pad)).astype(np.float32))
+    dy = full[:, : H * d].reshape(T, H, d)
+    ref = L.rope_backward_rows(dy, np.arange(T) + 7, 10000.0, layout)
+    buf = dev(full, "bf16")
+    dyv = buf.as_strided((T, H, d), (H * d + pad, d, 1))
+    dxv = torch.zeros_like(buf).as_strided((T, H, d), (H * d + pad, d, 1))
+    vtb.rope_bwd(dyv, pos0=7, layout=layout, dx=dxv)
+    torch.cuda.synchronize()
+    assert_close("rope bf16", host(dxv), ref, TOL["bf16"])
+
+
+def test_rope_bf16_in_place_positions():
+    need_gpu()
+    say("rope bf16 in place, explicit positions up to 8191")
+    rng = np.random.default_rng(11)
+    T, H, d = 37, 5, 128
+    dy = synth.bf16_round(rng.standard_normal((T, H, d)).astype(np.float32))
+    pos = np.sort(rng.integers(0, 8192, T)).astype(np.int32)
+    x = dev(dy, "bf16")
+    vtb.rope_bwd(x, pos=torch.from_numpy(pos).cuda(), dx=x)
+    torch.cuda.synchronize()
+    assert_close("rope bf16 in place", host(x), L.rope_backward_rows(dy, pos, 10000.0, 0), TOL["bf16"])
+
+
+@pytest.mark.parametrize("rows,n", [(3, 64), (17, 2560), (5, 5000), (4, 100)])
+def test_rmsnorm_bf16(rows, n):
+    need_gpu()
+    say(f"rmsnorm bf16 rows {rows} n {n}")
+    rng = np.random.default_rng(n + 1)
+    x = synth.bf16_round(rng.standard_normal((rows, n)).astype(np.float32))
+    dy = synth.bf16_round(rng.standard_normal((rows, n)).astype(np.float32))
+    g = rng.uniform(0.5, 1.5, n).astype(np.float32)
+    out = vtb.rmsnorm_bwd(dev(x, "bf16"), dev(g), dev(dy, "bf16"), 1e-6)
+    torch.cuda.synchronize()
+    assert_close("rmsnorm bf16", host(out), L.rmsnorm_backward_rows(x, g, dy, 1e-6), TOL["bf16"])

@@ -27,7 +27,8 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
     "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd", "attn_fwd_lse",
-    "rope_bwd", "rmsnorm_bwd", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd", "relu2_mul_bwd",
+    "rope_bwd", "rmsnorm_bwd", "rope_bwd_ex", "rmsnorm_bwd_ex", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd",
+    "relu2_mul_bwd",
     "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
     "attn_block_bwd_workspace_size", "attn_block_bwd",
 )
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P]),
         "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
         "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
+        "rope_bwd_ex": (ctypes.c_int, [I32, P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
+        "rmsnorm_bwd_ex": (ctypes.c_int, [I32, P, P, P, P, I32, I32, F32, P]),
         "rope_rmsnorm_res_bwd": (ctypes.c_int, [P, F32, P, P, P, P, I32, I32, I32, I32, F64, I32, F32, P]),
         "linear_bwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
         "layernorm_bwd": (ctypes.c_int, [I32, P, P, P, P, I32, I32, P]),
@@ -251,28 +254,41 @@ def attn_fwd_lse(q, k, scale: float, causal: bool, lse=None, stream=None):
 
 
 def rope_bwd(dy, pos=None, pos0: int = 0, base: float = 10000.0, layout: int = 0, dx=None, stream=None):
-    """R(-theta) on every pair of dy [n_tok, n_heads, head_dim] (fp32, heads packed)."""
-    if dy.dtype != torch.float32 or dy.dim() != 3 or dy.stride(2) != 1 or dy.stride(1) != dy.shape[2]:
-        raise ValueError("dy must be float32 [n_tok, n_heads, head_dim] with packed heads")
+    """R(-theta) on every pair of dy [n_tok, n_heads, head_dim] (fp32 or bf16, heads packed);
+    bf16 goes through rope_bwd_ex."""
+    if dy.dtype not in (torch.float32, torch.bfloat16) or dy.dim() != 3 or dy.stride(2) != 1 or dy.stride(1) != dy.shape[2]:
+        raise ValueError("dy must be float32 or bfloat16 [n_tok, n_heads, head_dim] with packed heads")
     dx = torch.empty_like(dy) if dx is None else dx
-    if dx.stride() != dy.stride():
-        raise ValueError("dx must have dy's strides")
+    if dx.stride() != dy.stride() or dx.dtype != dy.dtype or dx.shape != dy.shape:
+        raise ValueError("dx must have dy's shape, dtype and strides")
     if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
         raise TypeError("pos must be contiguous int32")
     n, h, d = dy.shape
-    _check(lib().rope_bwd(_ptr(dy), _ptr(dx), n, h, d, dy.stride(0), _ptr(pos), int(pos0), float(base), int(layout),
-                          _stream(stream)), "rope_bwd")
+    args = (_ptr(dy), _ptr(dx), n, h, d, dy.stride(0), _ptr(pos), int(pos0), float(base), int(layout), _stream(stream))
+    if dy.dtype == torch.float32:
+        _check(lib().rope_bwd(*args), "rope_bwd")
+    else:
+        _check(lib().rope_bwd_ex(VTB_BF16, *args), "rope_bwd_ex")
     return dx
 
 
 def rmsnorm_bwd(x, gamma, dy, eps: float = 1e-6, dx=None, stream=None):
-    """rmsNormBackward per row of x, dy [rows, n] (fp32 contiguous)."""
-    for t, nm in ((x, "x"), (gamma, "gamma"), (dy, "dy")):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise TypeError(f"{nm} must be contiguous float32")
+    """rmsNormBackward per row of x, dy [rows, n] (fp32 or bf16 contiguous; gamma fp32 [n]);
+    bf16 goes through rmsnorm_bwd_ex."""
+    if gamma.dtype != torch.float32 or not gamma.is_contiguous() or gamma.shape != (x.shape[-1],):
+        raise TypeError("gamma must be contiguous float32 [n]")
+    for t, nm in ((x, "x"), (dy, "dy")):
+        if t.dtype not in (torch.float32, torch.bfloat16) or t.dtype != x.dtype or not t.is_contiguous() or t.shape != x.shape:
+            raise TypeError(f"{nm} must be contiguous float32 or bfloat16, matching x")
     dx = torch.empty_like(x) if dx is None else dx
+    if dx.dtype != x.dtype or dx.shape != x.shape or not dx.is_contiguous():
+        raise TypeError("dx must be contiguous and match x")
     rows, n = x.shape
-    _check(lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), rows, n, float(eps), _stream(stream)), "rmsnorm_bwd")
+    args = (_ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), rows, n, float(eps), _stream(stream))
+    if x.dtype == torch.float32:
+        _check(lib().rmsnorm_bwd(*args), "rmsnorm_bwd")
+    else:
+        _check(lib().rmsnorm_bwd_ex(VTB_BF16, *args), "rmsnorm_bwd_ex")
     return dx
 
 

@@ -331,9 +331,10 @@ int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
   return hip_status(vtb::launch_flash_dq(p, vtb::ROW_FWD, s), "forward pass");
 }
 
-int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,
-             const int32_t* pos, int32_t pos0, double base, int32_t layout, vtb_stream_t stream) {
+int rope_bwd_ex(int32_t dtype, const void* dy, void* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim,
+                int64_t tok_stride, const int32_t* pos, int32_t pos0, double base, int32_t layout, vtb_stream_t stream) {
   g_last_error.clear();
+  if (!valid_dtype(dtype)) return fail(VTB_ERR_ARG, "dtype=%d", dtype);
   if (n_tok < 0 || n_heads < 1 || head_dim < 2 || (head_dim & 1))
     return fail(VTB_ERR_ARG, "bad shape n_tok=%d n_heads=%d head_dim=%d (head_dim must be even)", n_tok, n_heads, head_dim);
   if (tok_stride < (int64_t)n_heads * head_dim) return fail(VTB_ERR_ARG, "tok_stride < n_heads * head_dim");
@@ -341,28 +342,40 @@ int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t
   if (!(base > 0.0) || !std::isfinite(base)) return fail(VTB_ERR_ARG, "base must be positive and finite");
   if (n_tok == 0) return VTB_OK;
   if (!dy || !dx) return fail(VTB_ERR_ARG, "dy and dx must be non-NULL");
-  const size_t bytes = ((size_t)(n_tok - 1) * tok_stride + (size_t)n_heads * head_dim) * 4;
+  const size_t bytes = ((size_t)(n_tok - 1) * tok_stride + (size_t)n_heads * head_dim) * esize(dtype);
   if (dx != dy && overlap(span_of(dx, bytes), span_of(dy, bytes))) return fail(VTB_ERR_ALIAS, "dx partially overlaps dy");
   if (pos && (overlap(span_of(pos, n_tok * 4u), span_of(dx, bytes))))
     return fail(VTB_ERR_ALIAS, "pos overlaps dx");
-  return hip_status(vtb::launch_rope_bwd(dy, dx, n_tok, n_heads, head_dim, tok_stride, pos, pos0, base, layout,
-                                         reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(vtb::launch_rope_bwd(dtype == VTB_BF16, dy, dx, n_tok, n_heads, head_dim, tok_stride, pos, pos0, base,
+                                         layout, reinterpret_cast<hipStream_t>(stream)),
                     "rope_bwd");
 }
 
-int rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int32_t rows, int32_t n, float eps,
-                vtb_stream_t stream) {
+int rope_bwd(const float* dy, float* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim, int64_t tok_stride,
+             const int32_t* pos, int32_t pos0, double base, int32_t layout, vtb_stream_t stream) {
+  return rope_bwd_ex(VTB_F32, dy, dx, n_tok, n_heads, head_dim, tok_stride, pos, pos0, base, layout, stream);
+}
+
+int rmsnorm_bwd_ex(int32_t dtype, const void* x, const float* gamma, const void* dy, void* dx, int32_t rows, int32_t n,
+                   float eps, vtb_stream_t stream) {
   g_last_error.clear();
+  if (!valid_dtype(dtype)) return fail(VTB_ERR_ARG, "dtype=%d", dtype);
   if (rows < 0 || n < 1) return fail(VTB_ERR_ARG, "bad shape rows=%d n=%d", rows, n);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(VTB_ERR_ARG, "eps must be finite and >= 0");
   if (rows == 0) return VTB_OK;
   if (!x || !gamma || !dy || !dx) return fail(VTB_ERR_ARG, "x, gamma, dy and dx must be non-NULL");
-  const size_t bytes = (size_t)rows * n * 4;
+  const size_t bytes = (size_t)rows * n * esize(dtype);
   const Span o = span_of(dx, bytes);
   if (overlap(o, span_of(x, bytes)) || overlap(o, span_of(dy, bytes)) || overlap(o, span_of(gamma, (size_t)n * 4)))
     return fail(VTB_ERR_ALIAS, "dx overlaps an input");
-  return hip_status(vtb::launch_rmsnorm_bwd(x, gamma, dy, dx, rows, n, eps, reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(vtb::launch_rmsnorm_bwd(dtype == VTB_BF16, x, gamma, dy, dx, rows, n, eps,
+                                            reinterpret_cast<hipStream_t>(stream)),
                     "rmsnorm_bwd");
+}
+
+int rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int32_t rows, int32_t n, float eps,
+                vtb_stream_t stream) {
+  return rmsnorm_bwd_ex(VTB_F32, x, gamma, dy, dx, rows, n, eps, stream);
 }
 
 int rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const float* gamma, const float* dh_out,

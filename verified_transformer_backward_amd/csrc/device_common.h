@@ -38,6 +38,17 @@ template <> struct Frag<__bf16> { using type = bf16x8; };
 template <> struct Frag<float> { using type = f32x8; };
 template <typename E> using frag_t = typename Frag<E>::type;
 
+// 16 bytes of elements: 4 fp32 or 8 bf16, as one native vector.
+template <typename E> struct Vec16;
+template <> struct Vec16<float> {
+  using type = f32x4;
+  static constexpr int n = 4;
+};
+template <> struct Vec16<__bf16> {
+  using type = bf16x8;
+  static constexpr int n = 8;
+};
+
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename E> __device__ __forceinline__ E from_f32(float x);

@@ -56,7 +56,8 @@ __device__ __forceinline__ float2 block_sum2(float a, float b) {
 // ---------------------------------------------------------------------- RoPE backward
 // One thread per (token, pair index i); it rotates pair i of every head of the token
 // with one sin/cos, so the transcendental work is shared across heads.
-__global__ __launch_bounds__(256) void rope_bwd_kernel(const float* dy, float* dx, int n_tok,
+template <typename E>
+__global__ __launch_bounds__(256) void rope_bwd_kernel(const E* dy, E* dx, int n_tok,
                                                        int n_heads, int hd, int64_t tok_stride,
                                                        const int32_t* __restrict__ pos, int pos0, double base,
                                                        int layout) {
@@ -72,9 +73,9 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(const float* dy, float* d
     const int ib = layout == 0 ? 2 * i + 1 : i + half;
     for (int h = 0; h < n_heads; ++h) {
       const int64_t o = row + (int64_t)h * hd;
-      const float y0 = dy[o + ia], y1 = dy[o + ib];
-      dx[o + ia] = y0 * c + y1 * s;
-      dx[o + ib] = -y0 * s + y1 * c;
+      const float y0 = to_f32(dy[o + ia]), y1 = to_f32(dy[o + ib]);
+      dx[o + ia] = from_f32<E>(y0 * c + y1 * s);
+      dx[o + ib] = from_f32<E>(-y0 * s + y1 * c);
     }
   }
 }
@@ -83,19 +84,24 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(const float* dy, float* d
 // row is issued first; meanwhile the first head_dim/2 threads put the token's (cos, sin)
 // per frequency into LDS (angle formed and reduced in fp64, sin/cos in fp32), so each
 // angle is computed once per token and shared by all heads.
-// LAYOUT 0 pairs (2i, 2i+1): a float4 holds two pairs. LAYOUT 1 pairs (i, i + d/2): a unit
-// is the float4 at i and the float4 at i + d/2 of the same head, four pairs.
+// A 16-byte vector holds W = 4 (fp32) or 8 (bf16) elements. LAYOUT 0 pairs (2i, 2i+1): a
+// vector holds W/2 pairs. LAYOUT 1 pairs (i, i + d/2): a unit is the vector at i and the
+// vector at i + d/2 of the same head, W pairs.
 // dx == dy is allowed: a thread stores only what it loaded itself, after the barrier.
-template <int LAYOUT, int NV>
-__global__ __launch_bounds__(256) void rope_bwd_vec_kernel(const float4* dy, float4* dx, int n_heads, int hd,
-                                                           int64_t tok_stride4, const int32_t* __restrict__ pos,
+template <typename E, int LAYOUT, int NV>
+__global__ __launch_bounds__(256) void rope_bwd_vec_kernel(const E* dy_, E* dx_, int n_heads, int hd,
+                                                           int64_t tok_stride_v, const int32_t* __restrict__ pos,
                                                            int pos0, double log2_base) {
+  using V = typename Vec16<E>::type;
+  constexpr int W = Vec16<E>::n;
   extern __shared__ float2 cs[];   // [hd / 2] (cos, sin)
+  const V* dy = reinterpret_cast<const V*>(dy_);
+  V* dx = reinterpret_cast<V*>(dx_);
   const int t = blockIdx.x, tid = threadIdx.x;
-  const int hd4 = hd / 4, C4 = n_heads * hd4;
-  const int units = LAYOUT == 0 ? C4 : C4 / 2;
-  const int64_t ro = (int64_t)t * tok_stride4;
-  float4 a[NV], b[NV];
+  const int hdv = hd / W, Cv = n_heads * hdv;
+  const int units = LAYOUT == 0 ? Cv : Cv / 2;
+  const int64_t ro = (int64_t)t * tok_stride_v;
+  V a[NV], b[NV];
   int ia[NV], ib[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
@@ -103,9 +109,9 @@ __global__ __launch_bounds__(256) void rope_bwd_vec_kernel(const float4* dy, flo
     if (LAYOUT == 0) {
       ia[e] = ib[e] = u;
     } else {
-      const int h = u / (hd4 / 2), j = u % (hd4 / 2);
-      ia[e] = h * hd4 + j;
-      ib[e] = ia[e] + hd4 / 2;
+      const int h = u / (hdv / 2), j = u % (hdv / 2);
+      ia[e] = h * hdv + j;
+      ib[e] = ia[e] + hdv / 2;
     }
     a[e] = dy[ro + ia[e]];
     if (LAYOUT == 1) b[e] = dy[ro + ib[e]];
@@ -121,37 +127,41 @@ __global__ __launch_bounds__(256) void rope_bwd_vec_kernel(const float4* dy, flo
   for (int e = 0; e < NV; ++e) {
     if (tid + 256 * e >= units) continue;
     if (LAYOUT == 0) {
-      const int i0 = ((4 * ia[e]) % hd) / 2;
-      const float2 c0 = cs[i0], c1 = cs[i0 + 1];
-      const float4 y = a[e];
-      const float4 r = make_float4(y.x * c0.x + y.y * c0.y, -y.x * c0.y + y.y * c0.x, y.z * c1.x + y.w * c1.y,
-                                   -y.z * c1.y + y.w * c1.x);
-      nt_store4(&dx[ro + ia[e]], r);
-    } else {
-      const int i0 = 4 * (ia[e] % hd4);
-      const float ya[4] = {a[e].x, a[e].y, a[e].z, a[e].w}, yb[4] = {b[e].x, b[e].y, b[e].z, b[e].w};
-      float ra[4], rb[4];
+      const int i0 = ((W * ia[e]) % hd) / 2;
+      V r;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < W / 2; ++k) {
         const float2 c = cs[i0 + k];
-        ra[k] = ya[k] * c.x + yb[k] * c.y;
-        rb[k] = -ya[k] * c.y + yb[k] * c.x;
+        const float y0 = to_f32(a[e][2 * k]), y1 = to_f32(a[e][2 * k + 1]);
+        r[2 * k] = from_f32<E>(y0 * c.x + y1 * c.y);
+        r[2 * k + 1] = from_f32<E>(-y0 * c.y + y1 * c.x);
       }
-      nt_store4(&dx[ro + ia[e]], make_float4(ra[0], ra[1], ra[2], ra[3]));
-      nt_store4(&dx[ro + ib[e]], make_float4(rb[0], rb[1], rb[2], rb[3]));
+      __builtin_nontemporal_store(r, &dx[ro + ia[e]]);
+    } else {
+      const int i0 = W * (ia[e] % hdv);
+      V ra, rb;
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const float2 c = cs[i0 + k];
+        const float ya = to_f32(a[e][k]), yb = to_f32(b[e][k]);
+        ra[k] = from_f32<E>(ya * c.x + yb * c.y);
+        rb[k] = from_f32<E>(-ya * c.y + yb * c.x);
+      }
+      __builtin_nontemporal_store(ra, &dx[ro + ia[e]]);
+      __builtin_nontemporal_store(rb, &dx[ro + ib[e]]);
     }
   }
 }
 
 // ---------------------------------------------------------------------- RMSNorm backward
 // One 256-thread block per row; a row of up to 256*MAXE values stays in registers.
-template <int MAXE>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
-                                                          const float* __restrict__ dy, float* __restrict__ dx, int n,
+template <typename E, int MAXE>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const E* __restrict__ x, const float* __restrict__ gamma,
+                                                          const E* __restrict__ dy, E* __restrict__ dx, int n,
                                                           float eps) {
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * n;
-  const float* dyr = dy + row * n;
+  const E* xr = x + row * n;
+  const E* dyr = dy + row * n;
   float xv[MAXE], gv[MAXE];
   float ss = 0.f, cc = 0.f;
 #pragma unroll
@@ -160,8 +170,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
     xv[e] = 0.f;
     gv[e] = 0.f;
     if (idx < n) {
-      xv[e] = xr[idx];
-      gv[e] = dyr[idx] * gamma[idx];
+      xv[e] = to_f32(xr[idx]);
+      gv[e] = to_f32(dyr[idx]) * gamma[idx];
       ss = fmaf(xv[e], xv[e], ss);
       cc = fmaf(gv[e], xv[e], cc);
     }
@@ -173,28 +183,90 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
     const int idx = threadIdx.x + 256 * e;
-    if (idx < n) __builtin_nontemporal_store((gv[e] - xv[e] * coef) * rinv, &dx[row * n + idx]);
+    if (idx < n) __builtin_nontemporal_store(from_f32<E>((gv[e] - xv[e] * coef) * rinv), &dx[row * n + idx]);
   }
 }
 
-// Rows too long for registers: two passes over global memory.
-__global__ __launch_bounds__(256) void rmsnorm_bwd_long_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
-                                                               const float* __restrict__ dy, float* __restrict__ dx, int n,
-                                                               float eps) {
+// Vector form: one 256-thread block per row, 16-byte vectors of x and dy (W = 4 fp32 or 8
+// bf16 elements) held in registers between the two row sums and the store; gamma is read
+// as W fp32 values per vector. Vectors past the row end are clamped to its last vector and
+// masked out of the sums and stores, so every load is issued before the reduction.
+template <typename E, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_vec_kernel(const E* __restrict__ x, const float* __restrict__ gamma,
+                                                              const E* __restrict__ dy, E* __restrict__ dx, int n,
+                                                              float eps) {
+  using V = typename Vec16<E>::type;
+  constexpr int W = Vec16<E>::n;
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * n;
-  const float* dyr = dy + row * n;
+  const int nv = n / W;
+  const V* xr = reinterpret_cast<const V*>(x + row * n);
+  const V* dyr = reinterpret_cast<const V*>(dy + row * n);
+  V xv[NV], yv[NV];
+  float gv[NV][W];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int u = min((int)threadIdx.x + 256 * e, nv - 1);
+    xv[e] = xr[u];
+    yv[e] = dyr[u];
+#pragma unroll
+    for (int k = 0; k < W; k += 4) {
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(gamma + W * u + k);
+      gv[e][k] = g4[0];
+      gv[e][k + 1] = g4[1];
+      gv[e][k + 2] = g4[2];
+      gv[e][k + 3] = g4[3];
+    }
+  }
   float ss = 0.f, cc = 0.f;
-  for (int idx = threadIdx.x; idx < n; idx += 256) {
-    const float xe = xr[idx];
-    ss = fmaf(xe, xe, ss);
-    cc = fmaf(dyr[idx] * gamma[idx], xe, cc);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    if ((int)threadIdx.x + 256 * e < nv) {
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const float xe = to_f32(xv[e][k]);
+        gv[e][k] *= to_f32(yv[e][k]);
+        ss = fmaf(xe, xe, ss);
+        cc = fmaf(gv[e][k], xe, cc);
+      }
+    }
   }
   const float2 tot = block_sum2(ss, cc);
   const float r2 = tot.x / n + eps;
   const float rinv = rsqrtf(r2);
   const float coef = tot.y / (n * r2);
-  for (int idx = threadIdx.x; idx < n; idx += 256) dx[row * n + idx] = (dyr[idx] * gamma[idx] - xr[idx] * coef) * rinv;
+  V* dxr = reinterpret_cast<V*>(dx + row * n);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int u = (int)threadIdx.x + 256 * e;
+    if (u < nv) {
+      V o;
+#pragma unroll
+      for (int k = 0; k < W; ++k) o[k] = from_f32<E>((gv[e][k] - to_f32(xv[e][k]) * coef) * rinv);
+      __builtin_nontemporal_store(o, &dxr[u]);
+    }
+  }
+}
+
+// Rows too long for registers: two passes over global memory.
+template <typename E>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_long_kernel(const E* __restrict__ x, const float* __restrict__ gamma,
+                                                               const E* __restrict__ dy, E* __restrict__ dx, int n,
+                                                               float eps) {
+  const int64_t row = blockIdx.x;
+  const E* xr = x + row * n;
+  const E* dyr = dy + row * n;
+  float ss = 0.f, cc = 0.f;
+  for (int idx = threadIdx.x; idx < n; idx += 256) {
+    const float xe = to_f32(xr[idx]);
+    ss = fmaf(xe, xe, ss);
+    cc = fmaf(to_f32(dyr[idx]) * gamma[idx], xe, cc);
+  }
+  const float2 tot = block_sum2(ss, cc);
+  const float r2 = tot.x / n + eps;
+  const float rinv = rsqrtf(r2);
+  const float coef = tot.y / (n * r2);
+  for (int idx = threadIdx.x; idx < n; idx += 256)
+    dx[row * n + idx] = from_f32<E>((to_f32(dyr[idx]) * gamma[idx] - to_f32(xr[idx]) * coef) * rinv);
 }
 
 // ---------------------------------------------------------------------- fused layer tail
@@ -378,50 +450,82 @@ __global__ __launch_bounds__(256) void zero_bthd_kernel(E* x, int B, int T, int 
 
 int grid_for(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 8192)); }
 
-}  // namespace
-
-hipError_t launch_rope_bwd(const float* dy, float* dx, int n_tok, int n_heads, int head_dim, int64_t tok_stride,
-                           const int32_t* pos, int pos0, double base, int layout, hipStream_t s) {
+template <typename E>
+hipError_t rope_bwd_t(const E* dy, E* dx, int n_tok, int n_heads, int head_dim, int64_t tok_stride, const int32_t* pos,
+                      int pos0, double base, int layout, hipStream_t s) {
+  constexpr int W = Vec16<E>::n;
   const int64_t C = (int64_t)n_heads * head_dim;
-  const bool vec = (layout == 0 ? head_dim % 4 == 0 : head_dim % 8 == 0) && tok_stride % 4 == 0 && C / 4 <= 256 * 8 &&
-                   ((uintptr_t)dy | (uintptr_t)dx) % 16 == 0;
+  const bool vec = (layout == 0 ? head_dim % W == 0 : head_dim % (2 * W) == 0) && tok_stride % W == 0 &&
+                   C / W <= 256 * 8 && ((uintptr_t)dy | (uintptr_t)dx) % 16 == 0;
   if (vec) {
-    const int units = (int)(layout == 0 ? C / 4 : C / 8);
+    const int units = (int)(layout == 0 ? C / W : C / (2 * W));
     const int nv = (units + 255) / 256;
     const size_t lds = (size_t)(head_dim / 2) * sizeof(float2);
     const double l2b = std::log2(base);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(n_tok), dim3(256), lds, s, reinterpret_cast<const float4*>(dy),
-                         reinterpret_cast<float4*>(dx), n_heads, head_dim, tok_stride / 4, pos, pos0, l2b);
+      hipLaunchKernelGGL(kern, dim3(n_tok), dim3(256), lds, s, dy, dx, n_heads, head_dim, tok_stride / W, pos, pos0, l2b);
     };
     if (layout == 0) {
-      if (nv <= 1) go(rope_bwd_vec_kernel<0, 1>);
-      else if (nv <= 2) go(rope_bwd_vec_kernel<0, 2>);
-      else if (nv <= 4) go(rope_bwd_vec_kernel<0, 4>);
-      else go(rope_bwd_vec_kernel<0, 8>);
+      if (nv <= 1) go(rope_bwd_vec_kernel<E, 0, 1>);
+      else if (nv <= 2) go(rope_bwd_vec_kernel<E, 0, 2>);
+      else if (nv <= 4) go(rope_bwd_vec_kernel<E, 0, 4>);
+      else go(rope_bwd_vec_kernel<E, 0, 8>);
     } else {
-      if (nv <= 1) go(rope_bwd_vec_kernel<1, 1>);
-      else if (nv <= 2) go(rope_bwd_vec_kernel<1, 2>);
-      else if (nv <= 4) go(rope_bwd_vec_kernel<1, 4>);
-      else go(rope_bwd_vec_kernel<1, 8>);
+      if (nv <= 1) go(rope_bwd_vec_kernel<E, 1, 1>);
+      else if (nv <= 2) go(rope_bwd_vec_kernel<E, 1, 2>);
+      else if (nv <= 4) go(rope_bwd_vec_kernel<E, 1, 4>);
+      else go(rope_bwd_vec_kernel<E, 1, 8>);
     }
     return hipGetLastError();
   }
   const int64_t items = (int64_t)n_tok * (head_dim / 2);
-  hipLaunchKernelGGL(rope_bwd_kernel, dim3(grid_for(items)), dim3(256), 0, s, dy, dx, n_tok, n_heads, head_dim, tok_stride,
-                     pos, pos0, base, layout);
+  hipLaunchKernelGGL(rope_bwd_kernel<E>, dim3(grid_for(items)), dim3(256), 0, s, dy, dx, n_tok, n_heads, head_dim,
+                     tok_stride, pos, pos0, base, layout);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx, int rows, int n, float eps,
-                              hipStream_t s) {
+template <typename E>
+hipError_t rmsnorm_bwd_t(const E* x, const float* gamma, const E* dy, E* dx, int rows, int n, float eps, hipStream_t s) {
+  constexpr int W = Vec16<E>::n;
+  if (n % W == 0 && n <= 256 * W * 4 && ((uintptr_t)x | (uintptr_t)gamma | (uintptr_t)dy | (uintptr_t)dx) % 16 == 0) {
+    const int nv = (n / W + 255) / 256;
+    if (nv <= 1)
+      hipLaunchKernelGGL((rmsnorm_bwd_vec_kernel<E, 1>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    else if (nv <= 2)
+      hipLaunchKernelGGL((rmsnorm_bwd_vec_kernel<E, 2>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    else if (nv <= 3)
+      hipLaunchKernelGGL((rmsnorm_bwd_vec_kernel<E, 3>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    else
+      hipLaunchKernelGGL((rmsnorm_bwd_vec_kernel<E, 4>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    return hipGetLastError();
+  }
   if (n <= 256 * 4)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<4>, dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, 4>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
   else if (n <= 256 * 16)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<16>, dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<E, 16>), dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
   else
-    hipLaunchKernelGGL(rmsnorm_bwd_long_kernel, dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
+    hipLaunchKernelGGL(rmsnorm_bwd_long_kernel<E>, dim3(rows), dim3(256), 0, s, x, gamma, dy, dx, n, eps);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_bwd(int bf16, const void* dy, void* dx, int n_tok, int n_heads, int head_dim, int64_t tok_stride,
+                           const int32_t* pos, int pos0, double base, int layout, hipStream_t s) {
+  if (bf16)
+    return rope_bwd_t(static_cast<const __bf16*>(dy), static_cast<__bf16*>(dx), n_tok, n_heads, head_dim, tok_stride, pos,
+                      pos0, base, layout, s);
+  return rope_bwd_t(static_cast<const float*>(dy), static_cast<float*>(dx), n_tok, n_heads, head_dim, tok_stride, pos,
+                    pos0, base, layout, s);
+}
+
+hipError_t launch_rmsnorm_bwd(int bf16, const void* x, const float* gamma, const void* dy, void* dx, int rows, int n,
+                              float eps, hipStream_t s) {
+  if (bf16)
+    return rmsnorm_bwd_t(static_cast<const __bf16*>(x), gamma, static_cast<const __bf16*>(dy), static_cast<__bf16*>(dx),
+                         rows, n, eps, s);
+  return rmsnorm_bwd_t(static_cast<const float*>(x), gamma, static_cast<const float*>(dy), static_cast<float*>(dx), rows, n,
+                       eps, s);
 }
 
 hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x, const float* gamma,

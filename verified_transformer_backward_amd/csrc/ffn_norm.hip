@@ -20,17 +20,6 @@
 namespace vtb {
 namespace {
 
-// 16 bytes of elements: 4 fp32 or 8 bf16.
-template <typename E> struct Vec16;
-template <> struct Vec16<float> {
-  using type = f32x4;
-  static constexpr int n = 4;
-};
-template <> struct Vec16<__bf16> {
-  using type = bf16x8;
-  static constexpr int n = 8;
-};
-
 // Sum two values over a 256-thread block.
 __device__ __forceinline__ float2 block_sum2_256(float a, float b) {
   __shared__ float red[2][4];

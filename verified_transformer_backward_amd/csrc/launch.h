@@ -80,11 +80,12 @@ hipError_t launch_zero_bthd(void* x, int bf16, int B, int T, int H, int D, const
                             KernelEvents ev = {});
 
 // Elementwise tail.
-hipError_t launch_rope_bwd(const float* dy, float* dx, int n_tok, int n_heads, int head_dim,
-                           int64_t tok_stride, const int32_t* pos, int pos0, double base,
-                           int layout, hipStream_t s);
-hipError_t launch_rmsnorm_bwd(const float* x, const float* gamma, const float* dy, float* dx,
-                              int rows, int n, float eps, hipStream_t s);
+// RoPE and RMSNorm backward in fp32 or bf16 storage (bf16 != 0), fp32 arithmetic; gamma
+// stays fp32.
+hipError_t launch_rope_bwd(int bf16, const void* dy, void* dx, int n_tok, int n_heads, int head_dim,
+                           int64_t tok_stride, const int32_t* pos, int pos0, double base, int layout, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(int bf16, const void* x, const float* gamma, const void* dy, void* dx, int rows, int n,
+                              float eps, hipStream_t s);
 hipError_t launch_rope_rmsnorm_res_bwd(const float* dq, float dq_scale, const float* x,
                                        const float* gamma, const float* dh_out, float* dh_in, int T,
                                        int n_heads, int head_dim, int pos0, double base, int layout,
