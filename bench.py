@@ -591,13 +591,14 @@ def main():
             per["dq"].append(hip.ms(e[0], e[1]))             # start/end of each kernel's dispatch
             per["dkdv"].append(hip.ms(e[2], e[3]))
         hip.destroy(phase + [start, stop])
-        return total / nsteps, {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
+        spread = {k: [round(1e3 * float(np.percentile(v, q)), 2) for q in (10, 50, 90)] for k, v in per.items()}
+        return total / nsteps, {k: 1e3 * float(np.mean(v)) for k, v in per.items()}, spread
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    eager_ms, kern_us = timed(args.steps, nsets)          # per-pass times from eager steps
-    warm_eager_ms, warm_us = timed(max(10, args.steps // 2), 1)
+    eager_ms, kern_us, kern_spread = timed(args.steps, nsets)   # per-pass times from eager steps
+    warm_eager_ms, warm_us, _ = timed(max(10, args.steps // 2), 1)
     ms_step, same = graph_timed(args.steps, nsets)
     warm_ms, same_w = graph_timed(max(10, args.steps // 2), 1)
     if not (same and same_w):                             # graph replay must match eager calls
@@ -629,6 +630,7 @@ def main():
         "hbm_gbps": round(compulsory / (ms_step * 1e-3) / 1e9, 1),
         "frac_bf16_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "kernel_us_p10_p50_p90": kern_spread,
         "timing": "hip graph replay" if (same and same_w) else "eager",
         "eager_ms_per_step": round(eager_ms, 5),
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(flops / (warm_ms * 1e-3) / 1e12, 2),
