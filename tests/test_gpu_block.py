@@ -23,7 +23,7 @@ def _case(B, T, H, d, causal, seed):
 
 
 # B, T, H, d, causal: one tile, ragged token counts and widths, two sequences, no mask
-BLOCK_CASES = [(1, 16, 2, 8, True), (2, 37, 3, 12, True), (2, 64, 4, 32, False), (1, 100, 2, 64, True),
+BLOCK_CASES = [(2, 1, 2, 8, True), (1, 16, 2, 8, True), (2, 37, 3, 12, True), (2, 64, 4, 32, False), (1, 100, 2, 64, True),
                (3, 5, 1, 4, True), (1, 300, 2, 16, True)]
 
 

@@ -122,7 +122,7 @@ def _ffn_case(T, C, F, seed):
 
 # T, C, F: one tile, ragged tiles (widths not multiples of 4 or of the 64-wide tiles),
 # and sub-norm rows on both the vector and the any-width kernels
-FFN_CASES = [(16, 64, 96, 21), (37, 200, 300, 22), (50, 130, 75, 23), (64, 512, 8200, 24)]
+FFN_CASES = [(1, 64, 96, 20), (16, 64, 96, 21), (37, 200, 300, 22), (50, 130, 75, 23), (64, 512, 8200, 24)]
 
 
 @pytest.mark.parametrize("T,C,F,seed", FFN_CASES)

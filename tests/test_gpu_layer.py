@@ -161,7 +161,9 @@ def _layer_case(layer, T, H, d):
     return saved32, sc
 
 
-@pytest.mark.parametrize("T,H,d", [(64, 2, 64), (100, 3, 128)])
+# one token (every product has a single row or a one-deep contraction), a ragged shape and a
+# two-tile one
+@pytest.mark.parametrize("T,H,d", [(1, 2, 64), (64, 2, 64), (100, 3, 128)])
 def test_layer_bwd_small(T, H, d):
     need_gpu()
     say(f"layer_bwd T {T} H {H} d {d}")
