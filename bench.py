@@ -152,7 +152,7 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd",
+EXTRA_NAMES = ("single_query", "decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd",
                "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
@@ -210,6 +210,32 @@ def extra_workloads(torch, vtb, hip, only=None):
         if dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(synth.bf16_bits(a))).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    if want("single_query"):
+        # the single-head, single-query case: attention backward (q[64], K, V [16 x 64], no lse),
+        # RoPE backward on 32 pairs at position 5 and RMSNorm backward on n = 64, all fp32;
+        # a step is the three calls. Launch latency sets the time, so only us per step is reported.
+        x = synth.tiny_inputs()
+        t = {n: up(x[n]) for n in ("q", "k", "v", "dout")}
+        o = {n: torch.empty_like(t[n]) for n in ("q", "k", "v")}
+        desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], False, torch.float32, t["dout"], o["q"], o["k"], o["v"], t["v"])
+        ws = torch.empty(max(1, vtb.attn_bwd_workspace_size(desc)), dtype=torch.uint8, device=dev)
+        rdy, rx, rdy2, rg = up(x["rope_dy"]), up(x["rms_x"]), up(x["rms_dy"]), up(x["rms_gamma"])
+        rdx, rdx2 = torch.empty_like(rdy), torch.empty_like(rx)
+
+        def f():
+            st = torch.cuda.current_stream()
+            vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], False, dq=o["q"], dk=o["k"], dv=o["v"],
+                         workspace=ws, stream=st)
+            vtb.rope_bwd(rdy, pos0=x["rope_pos"], base=x["rope_base"], dx=rdx, stream=st)
+            vtb.rmsnorm_bwd(rx, rg, rdy2, eps=x["rms_eps"], dx=rdx2, stream=st)
+
+        ms = graph_ms(torch, hip, f, 50)
+        out["single_query"] = {"workload": "single-head single-query attention backward (Tk 16, d 64) + RoPE backward "
+                                           "(32 pairs) + RMSNorm backward (n 64), fp32",
+                               "ms": round(ms, 5), "value": round(ms * 1e3, 2), "unit": "us per step",
+                               "higher_is_better": False, "roofline": None}
+        del t, o, ws
 
     if want("decode_gqa"):
         # decode-shaped GQA: B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, no lse (HBM-bound: K, V in, dK, dV out)
