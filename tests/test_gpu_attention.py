@@ -138,6 +138,14 @@ CASES = [
     ("bf16_causal_gqa_Tq64_Tk160", 2, 64, 160, 8, 2, 128, "bf16", True),
     ("bf16_noncausal_T96", 1, 96, 96, 4, 4, 128, "bf16", False),
     ("bf16_causal_T224", 2, 224, 224, 3, 3, 128, "bf16", True),
+    # decode path limits: 16 query rows per kv head (the most it takes, its largest LDS use)
+    # with a ragged last chunk, in both head dims; more than 16 chunks (several chunk
+    # statistics per merging lane, dQ summed without the register prefetch); and 17 rows,
+    # one past the decode path, which the general kernels take
+    ("f32_decode_R16_causal_Tk300", 2, 2, 300, 16, 2, 128, "f32", True),
+    ("bf16_decode_R16_d64", 1, 4, 130, 8, 2, 64, "bf16", False),
+    ("f32_decode_Tk1100", 1, 1, 1100, 4, 1, 128, "f32", False),
+    ("f32_R17_past_decode", 1, 17, 90, 1, 1, 128, "f32", True),
 ]
 
 
