@@ -87,24 +87,27 @@ __device__ __forceinline__ void stage_rows(const AttnParams& p, int b, int kvh, 
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(AttnParams p, DecodeWs ws, int nch) {
-  // Chunk rows padded to D + 4 floats: a lane reading 16 bytes of its own key row and the
-  // 15 other lanes of its group reading theirs cover all 64 banks once.
+  // LDS rows padded to D + 4 floats: the 16 lanes of an MFMA operand read, each taking 16
+  // bytes of its own row, cover all 64 banks once.
   constexpr int LD = D + 4;
   constexpr int V = 16 / sizeof(E), CV = D / V, NL = kCH * CV / kThreads;   // 16-byte loads
   static_assert(NL * kThreads == kCH * CV, "chunk loads must tile the workgroup");
+  static_assert(kCH == 64 && kThreads == 256, "four waves of 16 keys cover the chunk");
   typedef E vec_t __attribute__((ext_vector_type(V)));
   const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = p.Hq / p.Hkv, R = G * p.Tq, Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
   const int j0 = ch * kCH;
-  // LDS sized for the group's R rows (chunk_lds_bytes): q, dO, the chunk (V, then K),
-  // then dP, e and e dP per row and key.
+  // Dynamic LDS sized for the group's R rows at launch: q and dO (rows of LD), the chunk
+  // (V, then K), then s and dP per row and key. Once the statistics of a row have read its
+  // s and dP, the same places take e and e dP (the lane that reads is the lane that writes).
   extern __shared__ float4 dyn4[];
   float* sq = reinterpret_cast<float*>(dyn4);
-  float* sdo = sq + R * D;
-  float* skv = sdo + R * D;
-  float* sdp = skv + kCH * LD;
-  float* sw = sdp + R * kCH;
-  float* sx = sw + R * kCH;
+  float* sdo = sq + R * LD;
+  float* skv = sdo + R * LD;
+  float* ss = skv + kCH * LD;
+  float* sdp = ss + R * kCH;
+  float* sw = ss;
+  float* sx = sdp;
   const int tid = threadIdx.x;
 
   // K and V of the chunk: every load issued up front, 16 contiguous bytes per lane; rows
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(AttnParams p, De
     kreg[i] = *reinterpret_cast<const vec_t*>(rp<E>(p.k, p.sk, b, j, kvh) + V * cv);
     vreg[i] = *reinterpret_cast<const vec_t*>(rp<E>(p.v, p.sv, b, j, kvh) + V * cv);
   }
-  stage_rows<E, D>(p, b, kvh, R, sq, sdo, D);
+  stage_rows<E, D>(p, b, kvh, R, sq, sdo, LD);
   auto to_lds = [&](const vec_t(&reg)[NL]) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -128,35 +131,43 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(AttnParams p, De
             make_float4(to_f32(reg[i][e4]), to_f32(reg[i][e4 + 1]), to_f32(reg[i][e4 + 2]), to_f32(reg[i][e4 + 3]));
     }
   };
-  // dot product of LDS row x (R-row array, stride D) with the lane's key row, four
-  // independent partial sums
-  auto dot = [&](const float* x, int jj) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // The chunk's products with every row on the fp32 matrix cores (16x16x4): wave w takes
+  // keys 16 w .. 16 w + 15 as the rows of A (the staged chunk) and the group's rows as the
+  // columns of B (x; columns past R re-read row R - 1 and are not stored), contracting over
+  // the head dim. Lane (c, g) = (lane % 16, lane / 16) holds d = d0 + 4 g .. 4 g + 3 of its
+  // A row and B column, and step e of each group of four contracts element e, so A and B
+  // agree on every k. Result register r is key 16 w + 4 g + r of row c: out[c][key] = mul * dot.
+  const int lane = tid & 63, w = tid >> 6, mc = lane & 15, mg = lane >> 4;
+  auto mfma_dots = [&](const float* x, float* out, float mul) {
+    const float* arow = skv + (16 * w + mc) * LD + 4 * mg;
+    const float* brow = x + min(mc, R - 1) * LD + 4 * mg;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int d = 0; d < D; d += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(skv + jj * LD + d);
-      const float4 xv = *reinterpret_cast<const float4*>(x + d);
-      acc.x = fmaf(xv.x, kv.x, acc.x);
-      acc.y = fmaf(xv.y, kv.y, acc.y);
-      acc.z = fmaf(xv.z, kv.z, acc.z);
-      acc.w = fmaf(xv.w, kv.w, acc.w);
+    for (int d0 = 0; d0 < D; d0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(arow + d0);
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(brow + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bx[e], acc, 0, 0, 0);
     }
-    return (acc.x + acc.y) + (acc.z + acc.w);
+    if (mc < R)
+      *reinterpret_cast<float4*>(out + mc * kCH + 16 * w + 4 * mg) =
+          make_float4(acc[0] * mul, acc[1] * mul, acc[2] * mul, acc[3] * mul);
   };
   to_lds(vreg);
   __syncthreads();
-
-  // lane = key jj, wave = rows rg, rg + 4, ...
-  const int jj = tid & 63, rg = tid >> 6, j = j0 + jj;
-  for (int r = rg; r < R; r += 4) sdp[r * kCH + jj] = dot(sdo + r * D, jj);
+  mfma_dots(sdo, sdp, 1.f);
   __syncthreads();   // every read of V is done
   to_lds(kreg);
   __syncthreads();
+  mfma_dots(sq, ss, p.scale);
+  __syncthreads();
 
+  // statistics: lane = key jj, wave = rows rg, rg + 4, ...
+  const int jj = lane, rg = w, j = j0 + jj;
   for (int r = rg; r < R; r += 4) {
     const int h = kvh * G + r / Tq, i = r % Tq;
     const int64_t row = ((int64_t)b * p.Hq + h) * Tq + i;
-    const float s = dot(sq + r * D, jj) * p.scale;
+    const float s = ss[r * kCH + jj];
     const float dp = sdp[r * kCH + jj];
     const bool vis = j < Tk && (!p.causal || j <= i + off);
     if (j < Tk) {
@@ -362,7 +373,7 @@ hipError_t decode_dispatch(const AttnParams& p, void* wsp, hipStream_t s, Kernel
   DecodeWs ws = carve(p, wsp);
   const dim3 grid(nch, p.Hkv, p.B);
   const int R = (p.Hq / p.Hkv) * p.Tq;
-  const size_t lds = (size_t)(2 * R * D + kCH * (D + 4) + 3 * R * kCH) * sizeof(float);   // <= 62 KB at R = 16
+  const size_t lds = (size_t)((2 * R + kCH) * (D + 4) + 2 * R * kCH) * sizeof(float);   // <= 59 KB at R = 16
   launch_kernel(decode_chunk_kernel<E, D>, grid, dim3(kThreads), (uint32_t)lds, s, e1, p, ws, nch);
   launch_kernel(decode_grads_kernel<E, EO, D>, grid, dim3(kThreads), 0, s, e2, p, ws, nch);
   return hipGetLastError();
