@@ -152,8 +152,8 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("single_query", "decode_gqa", "long_causal", "rope_rmsnorm_res", "rope_bwd", "rmsnorm_bwd", "layer_chain", "attn_fwd",
-               "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
+EXTRA_NAMES = ("single_query", "decode_gqa", "long_causal", "causal_train_f32out", "rope_rmsnorm_res", "rope_bwd",
+               "rmsnorm_bwd", "layer_chain", "attn_fwd", "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
 def copy_bandwidth(torch, hip):
@@ -288,6 +288,40 @@ def extra_workloads(torch, vtb, hip, only=None):
                            "roofline": {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                                         "algorithmic_flops": fl, "algorithmic_bytes": byts}}
         del t, o, lse
+
+    if want("causal_train_f32out"):
+        # the headline workload with fp32 outputs (bf16 in, fp32 accumulation, dQ/dK/dV fp32),
+        # 4 rotating input sets so the step does not find its data in the Infinity Cache
+        x = synth.causal_inputs()
+        base = {n: up(x[n], "bf16") for n in ("q", "k", "v", "dout")}
+        sets = []
+        for _ in range(4):
+            t = {n: v.clone() for n, v in base.items()}
+            t["lse"] = vtb.attn_fwd_lse(t["q"], t["k"], x["scale"], True)
+            t["o"] = [torch.empty(t[n].shape, dtype=torch.float32, device=dev) for n in ("q", "k", "v")]
+            desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], True, torch.float32, t["dout"], *t["o"], t["v"])
+            t["ws"] = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+            sets.append(t)
+        it = iter(range(10 ** 9))
+
+        def f():
+            t = sets[next(it) % 4]
+            vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], True, lse=t["lse"], out_dtype=torch.float32,
+                         dq=t["o"][0], dk=t["o"][1], dv=t["o"][2], workspace=t["ws"], stream=torch.cuda.current_stream())
+
+        ms = graph_ms(torch, hip, f, 20)
+        fl = 10 * 128 * 4 * 20 * 512 * 513 // 2
+        byts = 4 * base["q"].numel() * 2 + 4 * 20 * 512 * 4 + 3 * base["q"].numel() * 4
+        ceil = min(BF16_MFMA_PEAK_TFLOPS, fl / byts * HBM_PEAK_GBS / 1e3)
+        out["causal_train_f32out"] = {"workload": "causal attention backward B4 H20 T512 d128, bf16 in, fp32 out, lse given, "
+                                                  "4 rotating sets", "ms": round(ms, 5),
+                                      "value": round(fl / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                                      "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
+                                      "roofline": {"bound": "hbm", "ceiling_tflops": round(ceil, 1),
+                                                   "frac": round(fl / (ms * 1e-3) / 1e12 / ceil, 4),
+                                                   "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                                   "algorithmic_flops": fl, "algorithmic_bytes": byts}}
+        del sets, base
 
     if want("rope_rmsnorm_res") or want("rope_bwd") or want("rmsnorm_bwd"):
         # fused RoPE -> RMSNorm -> residual tail on the stack shape (30 x 256 rows, hidden 2560), fp32
@@ -463,6 +497,121 @@ def extra_workloads(torch, vtb, hip, only=None):
                               "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
                                            "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
                                            "algorithmic_flops": fl}}
+    return out
+
+
+def mfma_probe_rates(torch, hip):
+    """Sustained bf16 matrix-core rate on this GPU (libvtb_probe.so: independent MFMA
+    accumulations, operands in registers, no memory traffic), with the shader clock the
+    chip ran at meanwhile. Context beside the published peak, never a roofline denominator."""
+    import numpy as np
+
+    path = os.path.join(ROOT, "verified_transformer_backward_amd", "libvtb_probe.so")
+    L = ctypes.CDLL(path)
+    L.vtb_probe_mfma_bf16.restype = ctypes.c_int
+    L.vtb_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    blocks, iters = 256 * 2, 4096                        # two workgroups of 4 waves per CU: 2 waves per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    clk = torch.empty(blocks * 8, dtype=torch.int64, device="cuda:0")
+    sptr = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for shape, name, flop in ((0, "32x32x16", 32 * 32 * 16 * 2), (1, "16x16x32", 16 * 16 * 32 * 2)):
+        args = (shape, iters, blocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
+                ctypes.c_void_p(sptr))
+        if L.vtb_probe_mfma_bf16(*args) != 0:
+            raise RuntimeError("mfma probe launch failed")
+        torch.cuda.synchronize()
+        start, stop = hip.create(2)
+        hip.record(start, sptr)
+        if L.vtb_probe_mfma_bf16(*args) != 0:
+            raise RuntimeError("mfma probe launch failed")
+        hip.record(stop, sptr)
+        torch.cuda.synchronize()
+        ms = hip.ms(start, stop)
+        hip.destroy([start, stop])
+        c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.mean(c[:, 0]) / (np.mean(c[:, 1]) * 10.0))     # 100 MHz wall-clock ticks
+        total = 4.0 * iters * flop * blocks * 4
+        tf = total / (ms * 1e-3) / 1e12
+        out[f"bf16_{name}"] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+                               "frac_of_spec": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                               "per_clock_frac": round(tf * 1e12 / (256 * 4096 * ghz * 1e9), 4)}
+    del sink, clk
+    return out
+
+
+def oracle_per_config():
+    """The float64 oracle timed on each workload on this host, with every core BLAS uses and
+    (for the three smaller workloads) with one thread: a baseline only. Workloads too large to
+    run whole here are sampled and scaled to the full work (the sample is stated)."""
+    import numpy as np
+    import synth
+    from oracle import attention as A
+    from oracle import layer as Lr
+    from oracle import specs
+
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:                                   # no thread control: all-cores figures only
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    if threadpool_info is not None:
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+
+    def clock(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def pairs(B, H, Tq, Tk, causal):
+        return B * H * (Tq * (Tq + 1) // 2 + Tq * (Tk - Tq) if causal else Tq * Tk)
+
+    x1 = synth.tiny_inputs()
+
+    def c1():
+        A.attention_backward(x1["q"], x1["k"], x1["v"], x1["dout"], x1["scale"], False)
+        Lr.rope_backward_rows(x1["rope_dy"], np.array([x1["rope_pos"]]), x1["rope_base"])
+        specs.rmsnorm_backward(x1["rms_x"][0], x1["rms_gamma"], x1["rms_dy"][0], x1["rms_eps"])
+
+    x2 = synth.decode_gqa_inputs()
+    c2 = lambda: A.attention_backward(x2["q"], x2["k"], x2["v"], x2["dout"], x2["scale"], False)
+    x3 = synth.causal_inputs()
+    l3 = A.attention_lse(x3["q"], x3["k"], x3["scale"], True)
+    x4 = [Lr.layer_saved(**{k: v for k, v in synth.layer_inputs(l).items() if k != "W"}, W=synth.layer_inputs(l)["W"],
+                         H=20, scale=1.0 / np.sqrt(128.0)) for l in range(2)]
+    g4 = synth.layer_upstream_grad()
+    x5 = synth.long_causal_inputs()
+    h5 = [0, 1, 2, 3]
+    one5 = {n: x5[n][:, :, h5] for n in ("q", "k", "v", "dout")}
+    l5 = A.attention_lse(one5["q"], one5["k"], x5["scale"], True)
+
+    def c3(heads):
+        sub = {n: x3[n][:, :, :heads] for n in ("q", "k", "v", "dout")}
+        return lambda: A.attention_backward(sub["q"], sub["k"], sub["v"], sub["dout"], x3["scale"], True,
+                                            lse=l3[:, :heads])
+
+    work = {
+        "tiny_single_query": (10 * 64 * 16, c1, 1.0, "whole workload"),
+        "decode_gqa": (10 * 128 * pairs(8, 20, 1, 1024, False), c2, 1.0, "whole workload"),
+        "causal_train": (10 * 128 * pairs(4, 20, 512, 512, True), c3(20), 20 / 20, "whole workload (B4, all 20 heads)"),
+        "layer_chain": (30 * (4 * 256 * 2560 * 2560 + 8 * 128 * pairs(1, 20, 256, 256, True)),
+                        lambda: Lr.stack_backward(x4, g4, 20, 1.0 / np.sqrt(128.0)), 30 / 2,
+                        "2 of the 30 layers, scaled by 15"),
+        "long_causal": (10 * 128 * pairs(1, 32, 8192, 8192, True),
+                        lambda: A.attention_backward(one5["q"], one5["k"], one5["v"], one5["dout"], x5["scale"], True,
+                                                     lse=l5), 32 / len(h5), f"{len(h5)} of the 32 heads, scaled by 8"),
+    }
+    out = {"cores": int(cores), "kind": "oracle", "note": "float64 numpy oracle on the host; a baseline only"}
+    for name, (flops, fn, scale_up, sample) in work.items():
+        s = clock(fn) * scale_up
+        rec = {"seconds": round(s, 4), "gflops": round(flops / s / 1e9, 3), "sample": sample}
+        if name in ("tiny_single_query", "decode_gqa", "causal_train") and threadpool_limits is not None:
+            fn1, sc1, samp1 = (c3(4), 20 / 4, "4 of the 20 heads, scaled by 5") if name == "causal_train" else (fn, 1.0, sample)
+            with threadpool_limits(limits=1, user_api="blas"):
+                s1 = clock(fn1) * sc1
+            rec["one_thread"] = {"seconds": round(s1, 4), "gflops": round(flops / s1 / 1e9, 3), "sample": samp1}
+        out[name] = rec
     return out
 
 
@@ -655,6 +804,12 @@ def main():
                    "cache": f"cold: {nsets} rotating input/output sets" if nsets > 1 else "warm"},
         "hbm_gbps": round(compulsory / (ms_step * 1e-3) / 1e9, 1),
         "frac_bf16_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        # the whole step against its own roofline: min(MFMA peak, arithmetic intensity x HBM)
+        "step_roofline": {"achieved_tflops": round(tflops, 1),
+                          "intensity_flop_per_byte": round(flops / compulsory, 1),
+                          "ceiling_tflops": round(min(BF16_MFMA_PEAK_TFLOPS, flops / compulsory * HBM_PEAK_GBS / 1e3), 1),
+                          "frac": round(tflops / min(BF16_MFMA_PEAK_TFLOPS, flops / compulsory * HBM_PEAK_GBS / 1e3), 4),
+                          "compulsory_bytes": compulsory, "algorithmic_flops": flops},
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "kernel_us_p10_p50_p90": kern_spread,
         "timing": "hip graph replay" if (same and same_w) else "eager",
@@ -673,8 +828,10 @@ def main():
         out["other_workloads"] = extra_workloads(torch, vtb, hip)
         out["measured_hbm_copy"] = copy_bandwidth(torch, hip)
         out["measured_library_gemm"] = library_gemm_rates(torch, hip)
+        out["measured_mfma_probe"] = mfma_probe_rates(torch, hip)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        out["oracle_per_config"] = oracle_per_config()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -85,8 +85,10 @@ typedef struct {
 size_t attn_bwd_workspace_size(const attn_bwd_desc* desc);
 
 /* lse: NULL => computed internally from q, k. P: non-NULL => used as the softmax, and
- * lse is ignored. dq, dk, dv must all be non-NULL and must not overlap each other or any
- * input. Tk == 0 is an error; Tq == 0 (or B == 0) writes zero dk, dv. */
+ * lse is ignored. dq must be non-NULL; dk and dv may each be NULL, meaning that gradient
+ * is not wanted: it is not written (with both NULL the key-parallel pass is skipped).
+ * Outputs must not overlap each other or any input. Tk == 0 is an error; Tq == 0 (or
+ * B == 0) writes zero dk, dv (those that are non-NULL). */
 int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
              const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, vtb_stream_t stream);

@@ -76,6 +76,18 @@ def test_attn_bwd_validation_codes():
     assert b"stride" in L.vtb_last_error()
 
 
+def test_attn_bwd_dk_dv_are_optional():
+    # dk, dv NULL = not wanted: validation passes them (and reaches the workspace check,
+    # which fails here so that nothing launches); dq NULL is still an argument error
+    L = vtb.lib()
+    d = _desc()
+    assert L.attn_bwd(ctypes.byref(d), A0, A1, A2, A3, None, None, A4, None, None, WS, 16, None) == 4
+    assert L.attn_bwd(ctypes.byref(d), A0, A1, A2, A3, None, None, A4, A5, None, WS, 16, None) == 4
+    assert L.attn_bwd(ctypes.byref(d), A0, A1, A2, A3, None, None, A4, None, A6, WS, 16, None) == 4
+    assert L.attn_bwd(ctypes.byref(d), A0, A1, A2, A3, None, None, None, A5, A6, WS, 1 << 30, None) == 1
+    assert L.attn_bwd(ctypes.byref(d), A0, None, A2, A3, None, None, A4, None, None, WS, 1 << 30, None) == 1
+
+
 def test_attn_workspace_query():
     assert vtb.attn_bwd_workspace_size(_desc(D=96)) == 0
     d = _desc(B=4, Tq=512, Tk=512, Hq=20, Hkv=20, D=128, dtype=vtb.VTB_BF16)
@@ -104,6 +116,15 @@ def test_layer_validation_codes():
     cfg = vtb.make_layer_cfg(8, 2, 64, 0.1)
     assert L.layer_bwd(ctypes.byref(cfg), None, A0, A1, A2, A3, A4, WS, 1 << 30, None) == 1
     assert vtb.layer_bwd_workspace_size(cfg) > 0
+    # outputs and workspace are written with 16-byte vectors: unaligned ones are refused
+    sv = vtb.LayerSaved(A0, A1, A2, A3, A4, A5, A6, WS)
+    outs = [A0 + 0x1000000, A1 + 0x1000000, A2 + 0x1000000, A3 + 0x1000000, WS + 0x1000000]
+    for i in range(5):
+        o = list(outs)
+        o[i] += 4
+        rc = L.layer_bwd(ctypes.byref(cfg), ctypes.byref(sv), A6 + 0x1000000, o[0], o[1], o[2], o[3], o[4], 1 << 30, None)
+        assert rc == 2, (i, rc)
+        assert b"aligned" in L.vtb_last_error()
 
 
 def test_norm_ffn_validation_codes():

@@ -51,3 +51,66 @@ def test_layer_bwd_rejects_mismatched_shapes():
     sv["P"] = _f(H, T, T)
     with pytest.raises(ValueError, match="dk"):
         vtb.layer_bwd(sv, _f(T, C), 0.125, dk=_f(T, H, D + 1))
+
+
+def _attn(B=1, Tq=5, Tk=6, Hq=4, Hkv=2, D=64, dt=torch.bfloat16):
+    q = torch.zeros(B, Tq, Hq, D, dtype=dt)
+    k = torch.zeros(B, Tk, Hkv, D, dtype=dt)
+    return q, k, torch.zeros_like(k), torch.zeros_like(q)
+
+
+def test_attn_bwd_rejects_mismatched_tensors():
+    q, k, v, do = _attn()
+    bad = (ValueError, TypeError)
+    with pytest.raises(bad, match="v"):
+        vtb.attn_bwd(q, k, torch.zeros(1, 7, 2, 64, dtype=torch.bfloat16), do, 0.1, True)
+    with pytest.raises(bad, match="dout"):
+        vtb.attn_bwd(q, k, v, torch.zeros(1, 5, 4, 32, dtype=torch.bfloat16), 0.1, True)
+    with pytest.raises(bad, match="k"):
+        vtb.attn_bwd(q, torch.zeros(2, 6, 2, 64, dtype=torch.bfloat16), v, do, 0.1, True)
+    # an output whose dtype differs from out_dtype would be written at the wrong element size
+    with pytest.raises(bad, match="dq"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, out_dtype=torch.float32, dq=torch.zeros_like(q))
+    with pytest.raises(bad, match="dk"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, dk=torch.zeros(1, 6, 2, 32, dtype=torch.bfloat16))
+    with pytest.raises(bad, match="dv"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, out_dtype=torch.float32, dv=torch.zeros(1, 6, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(bad, match="lse"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, lse=torch.zeros(1, 4, 4))
+    with pytest.raises(bad, match="P"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, P=torch.zeros(1, 4, 5, 5))
+    with pytest.raises(bad, match="head dim"):
+        vtb.attn_bwd(q[..., ::2], k[..., ::2], v[..., ::2], do[..., ::2], 0.1, True)
+    with pytest.raises(bad, match="workspace"):
+        vtb.attn_bwd(q, k, v, do, 0.1, True, workspace=torch.zeros(16, dtype=torch.float32))
+
+
+def test_linear_bwd_rejects_mismatched_tensors():
+    x, w, dy = _f(4, 8), _f(8, 6), _f(4, 6)
+    bad = (ValueError, TypeError)
+    with pytest.raises(bad, match="w"):
+        vtb.linear_bwd(x, _f(7, 6), dy)
+    with pytest.raises(bad, match="dy"):
+        vtb.linear_bwd(x, w, _f(4, 5))
+    with pytest.raises(bad, match="dx"):
+        vtb.linear_bwd(x, w, dy, dx=_f(4, 9))
+    with pytest.raises(bad, match="dw"):
+        vtb.linear_bwd(x, w, dy, dw=_f(6, 8))
+    with pytest.raises(bad, match="x"):
+        vtb.linear_bwd(torch.zeros(4, 8, dtype=torch.bfloat16), w, dy)
+
+
+def test_rope_rmsnorm_res_bwd_rejects_mismatched_tensors():
+    T, H, D = 3, 2, 8
+    C = H * D
+    bad = (ValueError, TypeError)
+    with pytest.raises(bad, match="dh_out"):
+        vtb.rope_rmsnorm_res_bwd(_f(T, C), _f(T, C), _f(C), _f(T, C + 1), H, D)
+    with pytest.raises(bad, match="dq"):
+        vtb.rope_rmsnorm_res_bwd(_f(T + 1, C), _f(T, C), _f(C), _f(T, C), H, D)
+    with pytest.raises(bad, match="x"):
+        vtb.rope_rmsnorm_res_bwd(_f(T, C), _f(T, C - 1), _f(C), _f(T, C), H, D)
+    with pytest.raises(bad, match="gamma"):
+        vtb.rope_rmsnorm_res_bwd(_f(T, C), _f(T, C), _f(C + 2), _f(T, C), H, D)
+    with pytest.raises(bad, match="dh_in"):
+        vtb.rope_rmsnorm_res_bwd(_f(T, C), _f(T, C), _f(C), _f(T, C), H, D, dh_in=_f(T, C - 1))

@@ -231,6 +231,36 @@ def test_forward_single_key_copies_value(fwd):
     np.testing.assert_allclose(lse[0, :, 0], 0.3 * q[0, 0] @ k[0, 0, 0], rtol=1e-15)
 
 
+# Planted mistakes, each in a copy of the oracle's online forward built from its source on
+# the CPU: dropping the rescale of the value sum, of the exponential sum, or the maximum in
+# lse must each break the equality with the standard form.
+_ONLINE_MISTAKES = {
+    "no_value_rescale": ("u = u * a + e * v[b, j, kv]", "u = u + e * v[b, j, kv]"),
+    "no_sum_rescale": ("l = l * a + e", "l = l + e"),
+    "lse_without_max": ("lse[b, h, i] = m + np.log(l)", "lse[b, h, i] = np.log(l)"),
+}
+
+
+def _planted_online_forward(mistake):
+    import inspect
+    import textwrap
+
+    src = textwrap.dedent(inspect.getsource(A.attention_forward_online))
+    old, new = _ONLINE_MISTAKES[mistake]
+    assert src.count(old) == 1, mistake
+    ns = dict(vars(A))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    return ns["attention_forward_online"]
+
+
+@pytest.mark.parametrize("mistake", sorted(_ONLINE_MISTAKES))
+def test_online_forward_planted_mistakes_fail(mistake):
+    x = synth.attention_inputs(2, 7, 7, 2, 2, 8, seed=38)
+    O1, l1 = A.attention_forward(x["q"], x["k"], x["v"], 0.4, True)
+    O2, l2 = _planted_online_forward(mistake)(x["q"], x["k"], x["v"], 0.4, True)
+    assert not (np.allclose(O2, O1, rtol=1e-6, atol=1e-8) and np.allclose(l2, l1, rtol=1e-6, atol=1e-8))
+
+
 def test_online_forward_large_scores_stay_finite():
     # scores far beyond exp's range: the running maximum keeps every term finite
     x = synth.attention_inputs(1, 4, 4, 1, 1, 8, seed=34)

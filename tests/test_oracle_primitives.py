@@ -82,6 +82,34 @@ def test_rope_roundtrip_identity_at_tiny_workload_angles():
     assert np.max(np.abs(z0 - x0)) < 1e-14 and np.max(np.abs(z1 - x1)) < 1e-14
 
 
+def test_rope_roundtrip_check_rejects_a_rotation_that_is_not_the_inverse(monkeypatch):
+    # ropeRoundtripCheck must be able to fail: with the forward rotation R(+theta) planted
+    # where the inverse R(-theta) belongs, backward(forward(x)) = R(2 theta) x != x at the
+    # single-query workload's angles (pos 5: theta_0 = 5 rad, sin(10) != 0).
+    rng = np.random.default_rng(5)
+    th = specs.rope_angles([5], 64)[0]
+    x0, x1 = rng.standard_normal(32), rng.standard_normal(32)
+    assert specs.rope_roundtrip_check(x0, x1, th, tol=1e-6)
+    monkeypatch.setattr(specs, "rope_backward", specs.rope_forward)
+    assert not specs.rope_roundtrip_check(x0, x1, th, tol=1e-6)
+    # a plain sign error in the sine term (rotation by -theta applied twice) fails too
+    monkeypatch.setattr(specs, "rope_backward", lambda a, b, t: specs.rope_forward(a, b, -2.0 * np.asarray(t)))
+    assert not specs.rope_roundtrip_check(x0, x1, th, tol=1e-6)
+
+
+def test_run_all_checks_passes():
+    # runAllChecks ("Numerical Gradient Verification"): every verify* and the Tier-1
+    # identities hold for the oracle's backward specs.
+    assert verify.run_all_checks(verbose=False)
+
+
+def test_run_all_checks_fails_on_a_wrong_softmax_backward(monkeypatch):
+    # the same entry point must report a failure when one backward is wrong (negated)
+    right = specs.softmax_backward
+    monkeypatch.setattr(specs, "softmax_backward", lambda x, dy: -right(x, dy))
+    assert not verify.run_all_checks(verbose=False)
+
+
 def test_rope_backward_is_orthogonal():
     rng = np.random.default_rng(6)
     dy = rng.standard_normal((7, 3, 16))

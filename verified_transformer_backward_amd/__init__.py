@@ -195,27 +195,72 @@ def attn_bwd_workspace_size(desc: AttnBwdDesc) -> int:
     return int(lib().attn_bwd_workspace_size(ctypes.byref(desc)))
 
 
+def _same_device(t, ref, name: str):
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _check_given(t, shape, dtype, ref, name: str):
+    """A caller-given [B, T, H, D] output: its shape, dtype, device and a contiguous head dim."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    _same_device(t, ref, name)
+    _bthd_strides(t, name)
+
+
 def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dtype=None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
-    """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv).
+             dq=None, dk=None, dv=None, want_dk: bool = True, want_dv: bool = True, workspace=None, stream=None,
+             events=None):
+    """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv); dk (dv) is None when
+    want_dk (want_dv) is false, and the library then skips it.
 
     events: optional sequence of 4 hipEvent_t handles (ints): events[0]/[1] are recorded
     at the start/end of the call's first kernel, events[2]/[3] of its second
     (attn_bwd_timed)."""
     out_dtype = out_dtype or q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _bthd_strides(t, n)
     for t, n in ((k, "k"), (v, "v"), (dout, "dout")):
         if t.dtype != q.dtype or t.device != q.device:
             raise TypeError(f"{n} must match q's dtype and device")
-    dq = torch.empty(q.shape, dtype=out_dtype, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=out_dtype, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=out_dtype, device=q.device) if dv is None else dv
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dim")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError(f"dout {tuple(dout.shape)} must have q's shape {tuple(q.shape)}")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _check_given(dq, q.shape, out_dtype, q, "dq")
+    if not want_dk:
+        dk = None
+    elif dk is None:
+        dk = torch.empty(k.shape, dtype=out_dtype, device=q.device)
+    if not want_dv:
+        dv = None
+    elif dv is None:
+        dv = torch.empty(v.shape, dtype=out_dtype, device=q.device)
+    if dk is not None:
+        _check_given(dk, k.shape, out_dtype, q, "dk")
+    if dv is not None:
+        _check_given(dv, v.shape, out_dtype, q, "dv")
     desc = make_attn_desc(q, k, scale, causal, out_dtype, dout, dq, dk, dv, v)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise TypeError("lse must be contiguous float32 [B, Hq, Tq]")
-    if P is not None and (P.dtype != torch.float32 or not P.is_contiguous()):
-        raise TypeError("P must be contiguous float32 [B, Hq, Tq, Tk]")
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Tq):
+            raise TypeError(f"lse must be contiguous float32 {(B, Hq, Tq)}")
+        _same_device(lse, q, "lse")
+    if P is not None:
+        if P.dtype != torch.float32 or not P.is_contiguous() or tuple(P.shape) != (B, Hq, Tq, Tk):
+            raise TypeError(f"P must be contiguous float32 {(B, Hq, Tq, Tk)}")
+        _same_device(P, q, "P")
     if workspace is None:
         workspace = _workspace(attn_bwd_workspace_size(desc), q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    else:
+        _same_device(workspace, q, "workspace")
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(P),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
     if events is None:
@@ -294,12 +339,26 @@ def rmsnorm_bwd(x, gamma, dy, eps: float = 1e-6, dx=None, stream=None):
 
 def rope_rmsnorm_res_bwd(dq, x, gamma, dh_out, n_heads: int, head_dim: int, dq_scale: float = 1.0, pos0: int = 0,
                          base: float = 10000.0, layout: int = 0, eps: float = 1e-6, dh_in=None, stream=None):
-    """dh_in = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq_scale * dq)) per token row."""
+    """dh_in = dh_out + rmsNormBackward(x, gamma, ropeBackward(dq_scale * dq)) per token row.
+    x, dh_out, dh_in: [T, C] with C = n_heads * head_dim; dq: [T, C] or [T, n_heads, head_dim];
+    gamma: [C]. All contiguous float32 on one device."""
+    C = int(n_heads) * int(head_dim)
+    if dh_out.dim() != 2 or dh_out.shape[1] != C:
+        raise ValueError(f"dh_out must be [T, {C}] (n_heads * head_dim), got {tuple(dh_out.shape)}")
+    T = dh_out.shape[0]
+    shapes = {"dq": ((T, C), (T, n_heads, head_dim)), "x": ((T, C),), "gamma": ((C,),), "dh_out": ((T, C),)}
     for t, nm in ((dq, "dq"), (x, "x"), (gamma, "gamma"), (dh_out, "dh_out")):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError(f"{nm} must be contiguous float32")
-    dh_in = torch.empty_like(dh_out) if dh_in is None else dh_in
-    T = dh_out.shape[0]
+        if tuple(t.shape) not in shapes[nm]:
+            raise ValueError(f"{nm} must have shape {' or '.join(str(sh) for sh in shapes[nm])}, got {tuple(t.shape)}")
+        _same_device(t, dh_out, nm)
+    if dh_in is None:
+        dh_in = torch.empty_like(dh_out)
+    elif dh_in.dtype != torch.float32 or not dh_in.is_contiguous() or tuple(dh_in.shape) != (T, C):
+        raise ValueError(f"dh_in must be contiguous float32 {(T, C)}")
+    else:
+        _same_device(dh_in, dh_out, "dh_in")
     _check(lib().rope_rmsnorm_res_bwd(_ptr(dq), float(dq_scale), _ptr(x), _ptr(gamma), _ptr(dh_out), _ptr(dh_in), T,
                                       n_heads, head_dim, int(pos0), float(base), int(layout), float(eps),
                                       _stream(stream)), "rope_rmsnorm_res_bwd")
@@ -339,19 +398,33 @@ def relu2_mul_bwd(gate, up, dh, dgate=None, dup=None, stream=None):
 
 
 def linear_bwd(x, w, dy, want_dx: bool = True, want_dw: bool = True, dx=None, dw=None, stream=None):
-    """dX = dY W^T, dW = X^T dY for Y = X W (fp32 contiguous). Returns (dx, dw)."""
+    """dX = dY W^T, dW = X^T dY for Y = X W: x [T, K], w [K, N], dy [T, N], all contiguous
+    float32 on one device. Returns (dx [T, K], dw [K, N]); either is None when not wanted."""
     for t, nm in ((x, "x"), (w, "w"), (dy, "dy")):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise TypeError(f"{nm} must be contiguous float32")
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2:
+            raise TypeError(f"{nm} must be a contiguous float32 matrix")
+        _same_device(t, x, nm)
     T, K = x.shape
     N = w.shape[1]
-    if want_dx and dx is None:
-        dx = torch.empty((T, K), dtype=torch.float32, device=x.device)
-    if want_dw and dw is None:
-        dw = torch.empty((K, N), dtype=torch.float32, device=x.device)
-    _check(lib().linear_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx if want_dx else None), _ptr(dw if want_dw else None),
-                            T, K, N, _stream(stream)), "linear_bwd")
-    return (dx if want_dx else None), (dw if want_dw else None)
+    if w.shape[0] != K:
+        raise ValueError(f"w {tuple(w.shape)} must be [K, N] with K = {K} (x is {tuple(x.shape)})")
+    if tuple(dy.shape) != (T, N):
+        raise ValueError(f"dy must be {(T, N)}, got {tuple(dy.shape)}")
+    outs = []
+    for want, t, shape, nm in ((want_dx, dx, (T, K), "dx"), (want_dw, dw, (K, N), "dw")):
+        if not want:
+            outs.append(None)
+            continue
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=x.device)
+        elif t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"{nm} must be contiguous float32 {shape}")
+        else:
+            _same_device(t, x, nm)
+        outs.append(t)
+    dx, dw = outs
+    _check(lib().linear_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), T, K, N, _stream(stream)), "linear_bwd")
+    return dx, dw
 
 
 def make_layer_cfg(T, H, D, scale, eps=1e-6, rope_base=10000.0, rope_layout=0, causal=True) -> LayerBwdCfg:

@@ -179,15 +179,15 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   const Span sv = span_of(v, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_v, ein));
   const Span sdo = span_of(dout, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_do, ein));
   const Span sdq = span_of(dq, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_dq, eout));
-  const Span sdk = span_of(dk, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dk, eout));
-  const Span sdv = span_of(dv, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dv, eout));
+  const Span sdk = span_of(dk, dk ? bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dk, eout) : 0);
+  const Span sdv = span_of(dv, dv ? bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_dv, eout) : 0);
   const size_t rows = (size_t)d->B * d->Hq * d->Tq;
   const Span slse = span_of(lse, P ? 0 : (lse ? rows * 4 : 0));
   const Span sP = span_of(P, P ? rows * (size_t)d->Tk * 4 : 0);
   const Span sws = span_of(workspace, workspace_bytes);
   const bool has_q = d->B > 0 && d->Tq > 0, has_k = d->B > 0 && d->Tk > 0;
   if (has_q && (!q || !dout || !dq)) return fail(VTB_ERR_ARG, "q, dout and dq must be non-NULL");
-  if (has_k && (!k || !v || !dk || !dv)) return fail(VTB_ERR_ARG, "k, v, dk and dv must be non-NULL");
+  if (has_k && (!k || !v)) return fail(VTB_ERR_ARG, "k and v must be non-NULL");   // dk, dv: NULL = not wanted
   const void* ptrs[8] = {q, k, v, dout, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
@@ -214,9 +214,12 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
 
   if (!has_q) {  // no queries: dK = dV = 0
     if (!has_k) return VTB_OK;
-    rc = hip_status(vtb::launch_zero_bthd(dk, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dk, s, ev.pass(0)), "zero dk");
-    if (rc) return rc;
-    return hip_status(vtb::launch_zero_bthd(dv, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dv, s, ev.pass(1)), "zero dv");
+    if (dk) {
+      rc = hip_status(vtb::launch_zero_bthd(dk, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dk, s, ev.pass(0)), "zero dk");
+      if (rc) return rc;
+    }
+    if (dv) return hip_status(vtb::launch_zero_bthd(dv, p.out_bf16, d->B, d->Tk, d->Hkv, d->D, d->s_dv, s, ev.pass(1)), "zero dv");
+    return VTB_OK;
   }
 
   const size_t need = attn_bwd_workspace_size(d);
@@ -247,6 +250,7 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   else
     rc = hip_status(vtb::launch_flash_dq(p, mode, s, ev.pass(0)), "flash dq pass");
   if (rc) return rc;
+  if (!dk && !dv) return VTB_OK;   // only dQ wanted: the key-parallel pass is skipped
   if (mfma && !P) return hip_status(vtb::launch_mfma_dkdv(p, s, ev.pass(1)), "dk/dv pass");
   return hip_status(vtb::launch_flash_dkdv(p, s, ev.pass(1)), "flash dk/dv pass");
 }
@@ -476,6 +480,10 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   if (!dh_in || !dw || !dk || !dv) return fail(VTB_ERR_ARG, "outputs must be non-NULL");
   for (const float* ptr : in_ptrs)
     if (!aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  // the outputs and the workspace are written (and the workspace read back) with 16-byte vectors
+  const void* out_ptrs[5] = {dh_in, dw, dk, dv, workspace};
+  for (const void* ptr : out_ptrs)
+    if (ptr && !aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "outputs and workspace must be 16-byte aligned");
   const int T = c->T, H = c->H, D = c->D, C = H * D;
   const size_t TC = (size_t)T * C * 4;
   const Span ins[9] = {span_of(sv->x, TC), span_of(sv->gamma, (size_t)C * 4), span_of(sv->w, (size_t)C * C * 4),

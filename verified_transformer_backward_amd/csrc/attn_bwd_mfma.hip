@@ -841,8 +841,8 @@ void dkdv_mfma_kernel(AttnParams p) {
       for (int dt = 0; dt < kNDT; ++dt) {
         const f32x4 k4 = adK[dt][kt], v4 = adV[dt][kt];
         const float s = p.scale;
-        store4(p.dk, p.out_bf16, ok + 16 * dt, s * k4[0], s * k4[1], s * k4[2], s * k4[3]);
-        store4(p.dv, p.out_bf16, ov + 16 * dt, v4[0], v4[1], v4[2], v4[3]);
+        if (p.dk) store4(p.dk, p.out_bf16, ok + 16 * dt, s * k4[0], s * k4[1], s * k4[2], s * k4[3]);
+        if (p.dv) store4(p.dv, p.out_bf16, ov + 16 * dt, v4[0], v4[1], v4[2], v4[3]);
       }
     }
   }

@@ -319,14 +319,17 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
       EO* dvp = reinterpret_cast<EO*>(p.dv) + (int64_t)b * p.sdv[0] + (int64_t)j * p.sdv[1] + (int64_t)kvh * p.sdv[2] + 4 * c4;
       const float sc = p.scale;
       // dK and dV are written once and never read here: nontemporal stores
+      // (a null dK or dV is not wanted and not written)
       if constexpr (std::is_same<EO, float>::value) {
-        __builtin_nontemporal_store(f32x4{ak.x * sc, ak.y * sc, ak.z * sc, ak.w * sc}, reinterpret_cast<f32x4*>(dkp));
-        __builtin_nontemporal_store(f32x4{av.x, av.y, av.z, av.w}, reinterpret_cast<f32x4*>(dvp));
+        if (p.dk) __builtin_nontemporal_store(f32x4{ak.x * sc, ak.y * sc, ak.z * sc, ak.w * sc}, reinterpret_cast<f32x4*>(dkp));
+        if (p.dv) __builtin_nontemporal_store(f32x4{av.x, av.y, av.z, av.w}, reinterpret_cast<f32x4*>(dvp));
       } else {
-        __builtin_nontemporal_store(bf16x4{(__bf16)(ak.x * sc), (__bf16)(ak.y * sc), (__bf16)(ak.z * sc), (__bf16)(ak.w * sc)},
-                                    reinterpret_cast<bf16x4*>(dkp));
-        __builtin_nontemporal_store(bf16x4{(__bf16)av.x, (__bf16)av.y, (__bf16)av.z, (__bf16)av.w},
-                                    reinterpret_cast<bf16x4*>(dvp));
+        if (p.dk)
+          __builtin_nontemporal_store(bf16x4{(__bf16)(ak.x * sc), (__bf16)(ak.y * sc), (__bf16)(ak.z * sc), (__bf16)(ak.w * sc)},
+                                      reinterpret_cast<bf16x4*>(dkp));
+        if (p.dv)
+          __builtin_nontemporal_store(bf16x4{(__bf16)av.x, (__bf16)av.y, (__bf16)av.z, (__bf16)av.w},
+                                      reinterpret_cast<bf16x4*>(dvp));
       }
     }
   }

@@ -505,9 +505,9 @@ void flash_dkdv_kernel(AttnParams p) {
     __syncthreads();
     const int kl = lane >> 2;
     const int key = kb + 16 * w + kl;
-    if (key < Tk) {
+    void* base = which == 0 ? p.dk : p.dv;   // null: that gradient is not wanted
+    if (key < Tk && base) {
       const int64_t* st = which == 0 ? p.sdk : p.sdv;
-      void* base = which == 0 ? p.dk : p.dv;
       const int64_t o = (int64_t)b * st[0] + (int64_t)key * st[1] + (int64_t)kvh * st[2];
       const float* src = stage + kl * (D + 4);
       constexpr int PER = D / 4;
