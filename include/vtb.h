@@ -93,6 +93,21 @@ int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void
              const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
+/* attn_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid hipMalloc): identical arguments and results except
+ * that there is no workspace argument. The workspace is a device array inside the library,
+ * one per GPU, attn_bwd_noalloc_max_workspace() bytes (16 MiB), resolved on the first call
+ * on each device and held until the process ends; the call itself allocates nothing. The
+ * stream must belong to the current device. Calls whose attn_bwd_workspace_size exceeds
+ * the array return VTB_ERR_WORKSPACE (use attn_bwd with a caller workspace). Every call on
+ * a GPU uses that GPU's one array: calls that overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race and give undefined results. No part of
+ * the array needs clearing between calls: each call writes every value it reads first. */
+size_t attn_bwd_noalloc_max_workspace(void);
+int attn_bwd_noalloc(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
+                     const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
+                     vtb_stream_t stream);
+
 /* attn_bwd with per-kernel timing, for measurement: identical work and results. Every
  * call runs two kernels on `stream` (flash and MFMA paths: the query-parallel dq pass,
  * then the key-parallel dk/dv pass; decode path: the chunk pass, then the gradient pass;

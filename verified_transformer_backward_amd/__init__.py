@@ -26,7 +26,8 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
-    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_fwd", "attn_fwd_lse",
+    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace",
+    "attn_fwd", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_bwd_ex", "rmsnorm_bwd_ex", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd",
     "relu2_mul_bwd",
     "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "attn_bwd_timed": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P,
                                           ctypes.POINTER(ctypes.c_void_p), I32]),
+        "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P]),
+        "attn_bwd_noalloc_max_workspace": (SZ, []),
         "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
         "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P]),
         "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),

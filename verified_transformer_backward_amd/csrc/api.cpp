@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -263,6 +264,61 @@ int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
              const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
   return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
                        reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0});
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------- no-allocation variant
+// attn_bwd_noalloc's workspace: a file-scope device array, one copy per GPU, held until the
+// process ends. In host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, resolved on the first call on that device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(VTB_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(VTB_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return VTB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int attn_bwd_noalloc(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, const float* P, void* dq, void* dk, void* dv, vtb_stream_t stream) {
+  g_last_error.clear();
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  const size_t need = attn_bwd_workspace_size(d);
+  if (need > kScratchBytes)
+    return fail(VTB_ERR_WORKSPACE, "this problem needs %zu bytes of workspace; attn_bwd_noalloc holds at most %zu "
+                "(use attn_bwd with a caller workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, ws, kScratchBytes, reinterpret_cast<hipStream_t>(stream),
+                       PhaseEvents{nullptr, 0});
 }
 
 int attn_bwd_timed(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout,
