@@ -152,7 +152,7 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("single_query", "decode_gqa", "long_causal", "causal_train_f32out", "rope_rmsnorm_res", "rope_bwd",
+EXTRA_NAMES = ("single_query", "decode_gqa", "decode_fwd", "long_causal", "causal_train_f32out", "rope_rmsnorm_res", "rope_bwd",
                "rmsnorm_bwd", "layer_chain", "attn_fwd", "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
@@ -253,6 +253,33 @@ def extra_workloads(torch, vtb, hip, only=None):
                              "roofline": {"bound": "hbm", "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                           "algorithmic_bytes": byts}}
         del t, o, ws
+
+    if want("decode_fwd"):
+        # split-KV decode forward (O and lse) on the GQA decode shape, B8 Tq1 Hq20 Hkv5 Tk1024
+        # d128 fp32; 8 rotating input sets (336 MB of K and V) so that no call finds its K and
+        # V in the Infinity Cache. HBM-bound: K and V read once.
+        x = synth.decode_gqa_inputs()
+        base = {n: up(x[n]) for n in ("q", "k", "v")}
+        sets = []
+        for _ in range(8):
+            t = {n: v.clone() for n, v in base.items()}
+            t["o"] = torch.empty_like(t["q"])
+            t["lse"] = torch.empty((8, 20, 1), dtype=torch.float32, device=dev)
+            desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], False, torch.float32, dq=t["o"], v=t["v"])
+            t["ws"] = torch.empty(vtb.attn_fwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+            sets.append(t)
+        it = iter(range(10 ** 9))
+
+        def f():
+            t = sets[next(it) % 8]
+            vtb.attn_fwd(t["q"], t["k"], t["v"], x["scale"], False, o=t["o"], lse=t["lse"], workspace=t["ws"],
+                         stream=torch.cuda.current_stream())
+
+        ms = graph_ms(torch, hip, f, 40)
+        byts = sum(base[n].numel() * 4 for n in ("q", "k", "v")) + base["q"].numel() * 4 + 8 * 20 * 4
+        hbm_line("decode_fwd", "split-KV decode attention forward (O, lse) GQA B8 Tq1 Hq20 Hkv5 Tk1024 d128 fp32, "
+                               "8 rotating sets", ms, byts)
+        del sets, base
 
     if want("long_causal"):
         # long-context causal: B1 H32 T8192 d128 bf16, lse given (bf16 MFMA-bound)

@@ -143,6 +143,25 @@ int attn_fwd_lse(const attn_bwd_desc* desc, const void* q, const void* k, float*
 int attn_fwd(const attn_bwd_desc* desc, const void* q, const void* k, const void* v, void* o,
              float* lse, vtb_stream_t stream);
 
+/* Workspace bytes attn_fwd_ws needs for desc (>= 256); 0 when desc is invalid
+ * (vtb_last_error says why). */
+size_t attn_fwd_workspace_size(const attn_bwd_desc* desc);
+
+/* attn_fwd with a workspace, which lets decode-shaped problems ((Hq/Hkv) * Tq <= 16 rows
+ * per kv head) run split-KV: the tiled flash attention entry of the Hesper pull request's
+ * commit log computes, per KV tile in parallel, a partial output together with the
+ * tile's running maximum and sum of exponentials (Phase 1), then merges the tiles
+ * (Phase 2). Here one workgroup per (64-key chunk, kv head, batch) reads that chunk's K
+ * and V once for all rows of the group and writes (m_c, l_c, sum_j exp(s_j - m_c) v_j);
+ * a second kernel merges the chunks in order into O and lse. Results are those of
+ * attn_fwd (same definitions, same arguments) up to rounding order; other shapes take
+ * attn_fwd's own kernels and leave the workspace unused.
+ * workspace: device memory, 16-byte aligned, at least attn_fwd_workspace_size(desc)
+ * bytes (else VTB_ERR_WORKSPACE), owned by the caller, overwritten, not overlapping any
+ * tensor (VTB_ERR_ALIAS); NULL is VTB_ERR_WORKSPACE. Two kernels on `stream`. */
+int attn_fwd_ws(const attn_bwd_desc* desc, const void* q, const void* k, const void* v, void* o,
+                float* lse, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
+
 /* ---------------------------------------------------------------------------------------
  * RoPE backward: "Hesper.Training.VerifiedBackward", section "RoPE (Rotary Position
  * Embedding)", ropeBackward = rotation by -theta:

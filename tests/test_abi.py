@@ -95,6 +95,24 @@ def test_attn_workspace_query():
     assert n >= 2 * 4 * 20 * 512 * 4            # fp32 row term D and lse, one value per query row
 
 
+def test_attn_fwd_ws_validation_codes():
+    # decode shape (Hq/Hkv * Tq <= 16 rows per kv head): the split-KV forward needs a
+    # workspace of one fp32 D-vector and two statistics per (64-key chunk, query row)
+    L = vtb.lib()
+    d = _desc(B=8, Tq=1, Tk=1024, Hq=20, Hkv=5, D=128, causal=0)
+    need = L.attn_fwd_workspace_size(ctypes.byref(d))
+    rows, nch = 8 * 20 * 1, 1024 // 64
+    assert need >= nch * rows * (128 + 2) * 4
+    assert L.attn_fwd_workspace_size(ctypes.byref(_desc(D=96))) == 0
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, A2, A4, None, None, 1 << 30, None) == 4       # no workspace
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, A2, A4, None, WS, need - 256, None) == 4     # too small
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, A2, A4, None, A4, need, None) == 3           # ws overlaps o
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, A2, A4, None, A0, need, None) == 3           # ws overlaps q
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, A2, A4, None, WS + 8, need, None) == 2       # unaligned
+    assert L.attn_fwd_ws(ctypes.byref(_desc(D=96)), A0, A1, A2, A4, None, WS, need, None) == 2
+    assert L.attn_fwd_ws(ctypes.byref(d), A0, A1, None, A4, None, WS, need, None) == 1         # v NULL
+
+
 def test_elementwise_and_linear_validation_codes():
     L = vtb.lib()
     assert L.rope_bwd(A0, A1, 4, 2, 7, 14, None, 0, 10000.0, 0, None) == 1       # odd head_dim

@@ -27,7 +27,7 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
     "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace",
-    "attn_fwd", "attn_fwd_lse",
+    "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_ws", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_bwd_ex", "rmsnorm_bwd_ex", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd",
     "relu2_mul_bwd",
     "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
@@ -112,6 +112,8 @@ def lib() -> ctypes.CDLL:
         "attn_bwd_noalloc_max_workspace": (SZ, []),
         "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
         "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P]),
+        "attn_fwd_workspace_size": (SZ, [ctypes.POINTER(AttnBwdDesc)]),
+        "attn_fwd_ws": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, SZ, P]),
         "rope_bwd": (ctypes.c_int, [P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
         "rmsnorm_bwd": (ctypes.c_int, [P, P, P, P, I32, I32, F32, P]),
         "rope_bwd_ex": (ctypes.c_int, [I32, P, P, I32, I32, I32, I64, P, I32, F64, I32, P]),
@@ -198,6 +200,10 @@ def attn_bwd_workspace_size(desc: AttnBwdDesc) -> int:
     return int(lib().attn_bwd_workspace_size(ctypes.byref(desc)))
 
 
+def attn_fwd_workspace_size(desc: AttnBwdDesc) -> int:
+    return int(lib().attn_fwd_workspace_size(ctypes.byref(desc)))
+
+
 def _same_device(t, ref, name: str):
     if t.device != ref.device:
         raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
@@ -275,9 +281,11 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dt
 
 
 def attn_fwd(q, k, v, scale: float, causal: bool, out_dtype=None, o=None, lse=None, want_lse: bool = True,
-             stream=None):
+             split_kv: bool = True, workspace=None, stream=None):
     """Attention forward (see include/vtb.h): returns (o [B, Tq, Hq, D], lse [B, Hq, Tq] fp32
-    or None when want_lse is false and no lse tensor is given)."""
+    or None when want_lse is false and no lse tensor is given). split_kv (default) calls
+    attn_fwd_ws, whose decode-shaped problems run split-KV in a workspace (allocated here
+    when none is given); split_kv=False calls attn_fwd."""
     for t, n in ((k, "k"), (v, "v")):
         if t.dtype != q.dtype or t.device != q.device:
             raise TypeError(f"{n} must match q's dtype and device")
@@ -287,8 +295,19 @@ def attn_fwd(q, k, v, scale: float, causal: bool, out_dtype=None, o=None, lse=No
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     desc = make_attn_desc(q, k, scale, causal, out_dtype=o.dtype, dq=o, v=v)
-    _check(lib().attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
-           "attn_fwd")
+    if not split_kv:
+        _check(lib().attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
+               "attn_fwd")
+        return o, lse
+    need = attn_fwd_workspace_size(desc)
+    if need == 0:
+        _check(1, "attn_fwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or workspace.device != q.device or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor on q's device")
+    _check(lib().attn_fwd_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                             workspace.numel(), _stream(stream)), "attn_fwd_ws")
     return o, lse
 
 

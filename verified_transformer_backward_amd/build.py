@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libvtb.so")
 PROBE_LIB = os.path.join(HERE, "libvtb_probe.so")
 PROBE_SOURCES = ["probe_peak.hip"]
 
-SOURCES = ["api.cpp", "attn_flash_bwd.hip", "attn_bwd_mfma.hip", "attn_decode.hip", "elementwise.hip", "gemm_f32.hip", "ffn_norm.hip"]
+SOURCES = ["api.cpp", "attn_flash_bwd.hip", "attn_bwd_mfma.hip", "attn_decode.hip", "attn_decode_fwd.hip", "elementwise.hip", "gemm_f32.hip", "ffn_norm.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -351,8 +351,12 @@ int attn_fwd_lse(const attn_bwd_desc* d, const void* q, const void* k, float* ls
   return hip_status(vtb::launch_flash_dq(p, vtb::ROW_LSE_ONLY, reinterpret_cast<hipStream_t>(stream)), "lse pass");
 }
 
-int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
-             vtb_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int attn_fwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t s) {
   g_last_error.clear();
   int rc = check_desc(d, false);
   if (rc) return rc;
@@ -368,17 +372,19 @@ int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
   const size_t rows = (size_t)d->B * d->Hq * d->Tq;
   if (rows == 0) return VTB_OK;
   if (!q || !k || !v || !o) return fail(VTB_ERR_ARG, "q, k, v and o must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(VTB_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (workspace && !aligned16(workspace)))
+    return fail(VTB_ERR_UNSUPPORTED, "q, k, v, o and the workspace must be 16-byte aligned");
   const Span so = span_of(o, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_dq, eout));
   const Span sq = span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein));
   const Span sk = span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein));
   const Span sv = span_of(v, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_v, ein));
-  if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv)) return fail(VTB_ERR_ALIAS, "o overlaps q, k or v");
+  const Span sws = span_of(workspace, workspace_bytes);
+  if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv) || overlap(so, sws))
+    return fail(VTB_ERR_ALIAS, "o overlaps q, k, v or the workspace");
   if (lse) {
     const Span sl = span_of(lse, rows * 4);
-    if (overlap(sl, sq) || overlap(sl, sk) || overlap(sl, sv) || overlap(sl, so))
-      return fail(VTB_ERR_ALIAS, "lse overlaps q, k, v or o");
+    if (overlap(sl, sq) || overlap(sl, sk) || overlap(sl, sv) || overlap(sl, so) || overlap(sl, sws))
+      return fail(VTB_ERR_ALIAS, "lse overlaps q, k, v, o or the workspace");
   }
   vtb::AttnParams p = make_params(d);
   p.q = q;
@@ -386,9 +392,38 @@ int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
   p.v = v;
   p.dq = o;
   p.lse_out = lse;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (workspace && vtb::decode_fwd_applicable(p)) {
+    const size_t need = vtb::decode_fwd_workspace_bytes(p);
+    if (workspace_bytes < need)
+      return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (overlap(sws, sq) || overlap(sws, sk) || overlap(sws, sv))
+      return fail(VTB_ERR_ALIAS, "the workspace overlaps q, k or v");
+    return hip_status(vtb::launch_decode_fwd(p, workspace, s), "split-KV decode forward");
+  }
   if (vtb::mfma_fwd_applicable(p)) return hip_status(vtb::launch_mfma_fwd(p, s), "forward pass (MFMA)");
   return hip_status(vtb::launch_flash_dq(p, vtb::ROW_FWD, s), "forward pass");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
+             vtb_stream_t stream) {
+  return attn_fwd_impl(d, q, k, v, o, lse, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t attn_fwd_workspace_size(const attn_bwd_desc* d) {
+  if (check_desc(d, false) != VTB_OK) return 0;
+  const vtb::AttnParams p = make_params(d);
+  size_t bytes = vtb::decode_fwd_applicable(p) ? vtb::decode_fwd_workspace_bytes(p) : 0;
+  return std::max<size_t>(bytes, 256);
+}
+
+int attn_fwd_ws(const attn_bwd_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
+  if (!workspace) return fail(VTB_ERR_WORKSPACE, "attn_fwd_ws needs a workspace (attn_fwd_workspace_size)");
+  return attn_fwd_impl(d, q, k, v, o, lse, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
 int rope_bwd_ex(int32_t dtype, const void* dy, void* dx, int32_t n_tok, int32_t n_heads, int32_t head_dim,

@@ -73,6 +73,13 @@ bool decode_applicable(const AttnParams& p);
 hipError_t launch_decode(const AttnParams& p, void* ws, hipStream_t s, KernelEvents ev_chunk = {},
                          KernelEvents ev_grads = {});
 
+// Split-KV decode forward (Hq/Hkv * Tq <= 16): per 64-key chunk the rows' partial
+// (max, sum of exponentials, weighted value sum) in the workspace, then a merge into O
+// (written through dq / sdq) and lse (lse_out, when not null).
+bool decode_fwd_applicable(const AttnParams& p);
+size_t decode_fwd_workspace_bytes(const AttnParams& p);
+hipError_t launch_decode_fwd(const AttnParams& p, void* ws, hipStream_t s);
+
 // Fill `n` floats with zero (graph-capture safe, no hipMemsetAsync).
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s);
 // Zero a strided [B, T, H, D] tensor of fp32 or bf16 elements.
