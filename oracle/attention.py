@@ -149,12 +149,17 @@ def attention_lse(q, k, scale: float, causal: bool, row_block: int = 1024, q_hea
 
 
 def attention_backward(q, k, v, dout, scale: float, causal: bool, lse=None, P=None,
-                       kv_heads=None, row_block: int = 1024):
+                       kv_heads=None, row_block: int = 1024, O=None):
     """dQ, dK, dV of the attention output given dO (see the module docstring).
 
     P (the saved softmax) takes precedence; otherwise P_ij = exp(scale q_i.k_j - lse_i)
     with lse as given (not renormalised); with neither, lse is computed first.
     Entries of a given P at masked (invisible) positions are ignored.
+
+    O: the forward's output [B, Tq, Hq, d], when the caller saved it. Then the row term
+    is D_i = dO_i . O_i instead of rowsum(P o dP): with O_i = sum_j P_ij v_j the two are
+    equal (sum_j P_ij (dO_i . v_j) = dO_i . sum_j P_ij v_j), so an exact O changes nothing
+    and a rounded O enters only through D.
 
     kv_heads: optional list of kv-heads to compute; then dq holds only the q-heads of
     those groups ([B, Tq, len(kv_heads)*g, d], in group order) and dk, dv only those
@@ -189,7 +194,10 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool, lse=None, P=No
                         S = scale * (qi @ kk.T)
                         Pb = np.where(vis, np.exp(np.where(vis, S, 0.0) - _f64(lse[b, h, i0:i1])[:, None]), 0.0)
                     dP = doi @ vv.T
-                    D = np.sum(Pb * dP, axis=1, keepdims=True)
+                    if O is None:
+                        D = np.sum(Pb * dP, axis=1, keepdims=True)
+                    else:
+                        D = np.sum(doi * _f64(O[b, i0:i1, h, :]), axis=1, keepdims=True)
                     dS = Pb * (dP - D)
                     dq[b, i0:i1, ki * g + j, :] = scale * (dS @ kk)
                     dk[b, :kl, ki, :] += scale * (dS.T @ qi)

@@ -136,6 +136,41 @@ def test_row_dot_equals_do_dot_o():
     np.testing.assert_allclose(D, np.einsum("bihd,bihd->bhi", x["dout"].astype(np.float64), O), rtol=1e-12, atol=1e-13)
 
 
+def test_saved_o_row_term_matches_the_recomputed_one():
+    # With the forward's exact O, D_i = dO_i . O_i equals rowsum(P o dP): the backward is
+    # unchanged (GQA, causal, Tq < Tk).
+    x = synth.attention_inputs(2, 9, 13, 4, 2, 8, seed=21)
+    sc = 0.3
+    O, lse = A.attention_forward(x["q"], x["k"], x["v"], sc, causal=True)
+    ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True)
+    got = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True, lse=lse, O=O)
+    for r, g in zip(ref, got):
+        np.testing.assert_allclose(g, r, rtol=1e-11, atol=1e-12)
+
+
+def test_saved_o_enters_only_through_the_row_term():
+    # O = 0 makes D = 0, so dS = P o dP: brute force over every (row, key) pair with
+    # dQ_i = scale sum_j P_ij (dO_i . v_j) k_j and dV_j = sum_i P_ij dO_i (dV does not see D).
+    x = synth.attention_inputs(1, 5, 5, 2, 1, 4, seed=22)
+    sc = 0.5
+    _, lse, P = A.attention_forward(x["q"], x["k"], x["v"], sc, causal=True, want_p=True)
+    dq, dk, dv = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True, lse=lse,
+                                      O=np.zeros_like(x["q"]))
+    q, k, v, do = (x[n].astype(np.float64) for n in ("q", "k", "v", "dout"))
+    want_dq = np.zeros_like(dq)
+    want_dk = np.zeros_like(dk)
+    for h in range(2):
+        for i in range(5):
+            for j in range(i + 1):
+                ds = P[0, h, i, j] * float(do[0, i, h] @ v[0, j, 0])
+                want_dq[0, i, h] += sc * ds * k[0, j, 0]
+                want_dk[0, j, 0] += sc * ds * q[0, i, h]
+    np.testing.assert_allclose(dq, want_dq, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk, want_dk, rtol=1e-12, atol=1e-14)
+    _, _, dv_ref = A.attention_backward(x["q"], x["k"], x["v"], x["dout"], sc, causal=True, lse=lse)
+    np.testing.assert_allclose(dv, dv_ref, rtol=1e-12, atol=1e-14)
+
+
 def test_gqa_equals_mha_on_replicated_caches():
     x = synth.attention_inputs(2, 7, 9, 6, 2, 8, seed=9)
     g = 3
