@@ -152,7 +152,7 @@ def graph_ms(torch, hip, fn, reps):
     return ms
 
 
-EXTRA_NAMES = ("single_query", "decode_gqa", "decode_fwd", "long_causal", "causal_train_f32out", "rope_rmsnorm_res", "rope_bwd",
+EXTRA_NAMES = ("single_query", "decode_gqa", "decode_fwd", "long_causal", "causal_train_f32out", "causal_train_saved_o", "rope_rmsnorm_res", "rope_bwd",
                "rmsnorm_bwd", "layer_chain", "attn_fwd", "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
 
 
@@ -348,6 +348,39 @@ def extra_workloads(torch, vtb, hip, only=None):
                                                    "frac": round(fl / (ms * 1e-3) / 1e12 / ceil, 4),
                                                    "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                                                    "algorithmic_flops": fl, "algorithmic_bytes": byts}}
+        del sets, base
+
+    if want("causal_train_saved_o"):
+        # the headline workload for callers that saved the forward's O (attn_bwd_o): the row
+        # term is dO . O, so the query pass takes three contractions per key block; 8 rotating
+        # sets, O and lse from the library's own forward (untimed)
+        x = synth.causal_inputs()
+        base = {n: up(x[n], "bf16") for n in ("q", "k", "v", "dout")}
+        sets = []
+        for _ in range(8):
+            t = {n: v.clone() for n, v in base.items()}
+            t["o"], t["lse"] = vtb.attn_fwd(t["q"], t["k"], t["v"], x["scale"], True)
+            t["g"] = [torch.empty_like(t[n]) for n in ("q", "k", "v")]
+            desc = vtb.make_attn_desc(t["q"], t["k"], x["scale"], True, torch.bfloat16, t["dout"], *t["g"], t["v"])
+            t["ws"] = torch.empty(vtb.attn_bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+            sets.append(t)
+        it = iter(range(10 ** 9))
+
+        def f():
+            t = sets[next(it) % 8]
+            vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], x["scale"], True, lse=t["lse"], o=t["o"], dq=t["g"][0],
+                         dk=t["g"][1], dv=t["g"][2], workspace=t["ws"], stream=torch.cuda.current_stream())
+
+        ms = graph_ms(torch, hip, f, 40)
+        fl = 10 * 128 * 4 * 20 * 512 * 513 // 2      # the same counted work as the headline
+        byts = 5 * base["q"].numel() * 2 + 4 * 20 * 512 * 4 + 3 * base["q"].numel() * 2
+        out["causal_train_saved_o"] = {"workload": "causal attention backward B4 H20 T512 d128 bf16 with saved O and lse "
+                                                   "(attn_bwd_o), 8 rotating sets", "ms": round(ms, 5),
+                                       "value": round(fl / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                                       "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
+                                       "roofline": {"bound": "mfma",
+                                                    "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                                    "algorithmic_flops": fl, "algorithmic_bytes": byts}}
         del sets, base
 
     if want("rope_rmsnorm_res") or want("rope_bwd") or want("rmsnorm_bwd"):

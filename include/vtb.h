@@ -93,6 +93,22 @@ int attn_bwd(const attn_bwd_desc* desc, const void* q, const void* k, const void
              const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
+/* attn_bwd for callers that saved the forward's output O. "Hesper.Training.VerifiedBackward",
+ * section "Attention (full single-head)": the apply step gives O_i = sum_j P_ij v_j and
+ * dP_ij = dO_i . v_j, so the softmax backward's row term rowsum(P o dP) equals dO_i . O_i.
+ * That dot product (one fp32 sum per query row) replaces the pass over every visible key
+ * that attn_bwd needs for it: the query-parallel pass then forms dS = P o (dP - D)
+ * directly (three contractions per key block instead of four) and the key-parallel pass
+ * reads the same D. Results are attn_bwd's up to the rounding of O.
+ * o: [B, Tq, Hq, D] in desc->in_dtype, device memory, 16-byte aligned, with element
+ * strides s_o[3] (batch, token, head; multiples of 8), read only. lse is required and
+ * there is no saved P; every other argument is attn_bwd's (same workspace size).
+ * Decode-shaped problems (the decode path of attn_bwd) do not read o: their row term
+ * comes from the chunk statistics, which cost no extra K/V read. */
+int attn_bwd_o(const attn_bwd_desc* desc, const void* q, const void* k, const void* v,
+               const void* dout, const void* o, const int64_t* s_o, const float* lse, void* dq,
+               void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
+
 /* attn_bwd for callers that cannot allocate device memory (code under HIP graph capture,
  * serving loops, harnesses that forbid hipMalloc): identical arguments and results except
  * that there is no workspace argument. The workspace is a device array inside the library,

@@ -88,6 +88,27 @@ def test_attn_bwd_dk_dv_are_optional():
     assert L.attn_bwd(ctypes.byref(d), A0, None, A2, A3, None, None, A4, None, None, WS, 1 << 30, None) == 1
 
 
+def test_attn_bwd_o_validation_codes():
+    # a saved O needs lse; o's strides are checked like every other tensor's; o is an input
+    L = vtb.lib()
+    d = _desc()
+    so = (ctypes.c_int64 * 3)(8 * 2 * 64, 2 * 64, 64)
+    LSE, O = A6 + 0x1000000, WS + 0x1000000
+
+    def call(o=O, s_o=so, lse=LSE, dq=A4, ws=WS, wsb=1 << 20):
+        return L.attn_bwd_o(ctypes.byref(d), A0, A1, A2, A3, o, s_o, lse, dq, A5, A6, ws, wsb, None)
+
+    assert call(o=None) == 1
+    assert call(lse=None) == 1
+    assert call(s_o=None) == 1
+    bad = (ctypes.c_int64 * 3)(8 * 2 * 64, 2 * 64, 60)
+    assert call(s_o=bad) == 2
+    assert call(o=O + 8) == 2                              # unaligned
+    assert call(dq=O) == 3                                 # dq overlaps o
+    assert call(ws=O) == 3                                 # workspace overlaps o
+    assert call(wsb=16) == 4
+
+
 def test_attn_workspace_query():
     assert vtb.attn_bwd_workspace_size(_desc(D=96)) == 0
     d = _desc(B=4, Tq=512, Tk=512, Hq=20, Hkv=20, D=128, dtype=vtb.VTB_BF16)

@@ -26,7 +26,7 @@ _STATUS = {0: "VTB_OK", 1: "VTB_ERR_ARG", 2: "VTB_ERR_UNSUPPORTED", 3: "VTB_ERR_
 
 EXPORTS = (
     "vtb_status_string", "vtb_last_error", "vtb_abi_version",
-    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_timed", "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace",
+    "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_o", "attn_bwd_timed", "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace",
     "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_ws", "attn_fwd_lse",
     "rope_bwd", "rmsnorm_bwd", "rope_bwd_ex", "rmsnorm_bwd_ex", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd",
     "relu2_mul_bwd",
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
         "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "attn_bwd_timed": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P, SZ, P,
                                           ctypes.POINTER(ctypes.c_void_p), I32]),
+        "attn_bwd_o": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, ctypes.POINTER(I64), P, P, P, P, P,
+                                      SZ, P]),
         "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P, P, P, P, P, P, P]),
         "attn_bwd_noalloc_max_workspace": (SZ, []),
         "attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(AttnBwdDesc), P, P, P, P]),
@@ -219,9 +221,12 @@ def _check_given(t, shape, dtype, ref, name: str):
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dtype=None,
              dq=None, dk=None, dv=None, want_dk: bool = True, want_dv: bool = True, workspace=None, stream=None,
-             events=None):
+             events=None, o=None):
     """dQ, dK, dV of attention (see include/vtb.h). Returns (dq, dk, dv); dk (dv) is None when
     want_dk (want_dv) is false, and the library then skips it.
+
+    o: the forward's saved output [B, Tq, Hq, D] (q's dtype and device, any strides with a
+    contiguous head dim); then attn_bwd_o runs, which needs lse and takes no P.
 
     events: optional sequence of 4 hipEvent_t handles (ints): events[0]/[1] are recorded
     at the start/end of the call's first kernel, events[2]/[3] of its second
@@ -270,6 +275,17 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool, lse=None, P=None, out_dt
         raise TypeError("workspace must be a contiguous uint8 tensor")
     else:
         _same_device(workspace, q, "workspace")
+    if o is not None:
+        if events is not None:
+            raise ValueError("events are not taken with a saved o")
+        if o.dtype != q.dtype or tuple(o.shape) != tuple(q.shape):
+            raise TypeError(f"o must have q's dtype and shape {tuple(q.shape)}")
+        _same_device(o, q, "o")
+        so = (ctypes.c_int64 * 3)(*_bthd_strides(o, "o"))
+        _check(lib().attn_bwd_o(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), so, _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
+               "attn_bwd_o")
+        return dq, dk, dv
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(P),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
     if events is None:

@@ -168,12 +168,23 @@ struct PhaseEvents {
   }
 };
 
+// o (with strides so): the forward's saved output, or NULL. When given, lse is required,
+// P must be NULL, and the row term D comes from dO . O.
 int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t s,
-                  PhaseEvents ev) {
+                  PhaseEvents ev, const void* o = nullptr, const int64_t* so = nullptr) {
   g_last_error.clear();
   int rc = check_desc(d, true);
   if (rc) return rc;
+  if (o) {
+    if (!so) return fail(VTB_ERR_ARG, "s_o is NULL");
+    if (P) return fail(VTB_ERR_ARG, "a saved O is used with lse, not with a saved P");
+    if (!lse && d->B > 0 && d->Tq > 0) return fail(VTB_ERR_ARG, "a saved O needs the saved lse");
+    for (int i = 0; i < 3; ++i) {
+      if (so[i] < 0) return fail(VTB_ERR_ARG, "o stride %d is negative", i);
+      if (so[i] % 8) return fail(VTB_ERR_UNSUPPORTED, "o stride %d = %lld is not a multiple of 8 elements", i, (long long)so[i]);
+    }
+  }
   const size_t ein = esize(d->in_dtype), eout = esize(d->out_dtype);
   const Span sq = span_of(q, bthd_bytes(d->B, d->Tq, d->Hq, d->D, d->s_q, ein));
   const Span sk = span_of(k, bthd_bytes(d->B, d->Tk, d->Hkv, d->D, d->s_k, ein));
@@ -186,21 +197,23 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   const Span slse = span_of(lse, P ? 0 : (lse ? rows * 4 : 0));
   const Span sP = span_of(P, P ? rows * (size_t)d->Tk * 4 : 0);
   const Span sws = span_of(workspace, workspace_bytes);
+  const Span so_ = span_of(o, o ? bthd_bytes(d->B, d->Tq, d->Hq, d->D, so, ein) : 0);
   const bool has_q = d->B > 0 && d->Tq > 0, has_k = d->B > 0 && d->Tk > 0;
   if (has_q && (!q || !dout || !dq)) return fail(VTB_ERR_ARG, "q, dout and dq must be non-NULL");
+  if (o && !aligned16(o)) return fail(VTB_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
   if (has_k && (!k || !v)) return fail(VTB_ERR_ARG, "k and v must be non-NULL");   // dk, dv: NULL = not wanted
   const void* ptrs[8] = {q, k, v, dout, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
   const Span outs[3] = {sdq, sdk, sdv};
-  const Span ins[7] = {sq, sk, sv, sdo, slse, sP, sws};
-  for (int o = 0; o < 3; ++o) {
-    for (int i = 0; i < 7; ++i)
-      if (overlap(outs[o], ins[i])) return fail(VTB_ERR_ALIAS, "output %d overlaps an input or the workspace", o);
-    for (int o2 = o + 1; o2 < 3; ++o2)
-      if (overlap(outs[o], outs[o2])) return fail(VTB_ERR_ALIAS, "outputs %d and %d overlap", o, o2);
+  const Span ins[8] = {sq, sk, sv, sdo, slse, sP, so_, sws};
+  for (int t = 0; t < 3; ++t) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[t], ins[i])) return fail(VTB_ERR_ALIAS, "output %d overlaps an input or the workspace", t);
+    for (int t2 = t + 1; t2 < 3; ++t2)
+      if (overlap(outs[t], outs[t2])) return fail(VTB_ERR_ALIAS, "outputs %d and %d overlap", t, t2);
   }
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 7; ++i)
     if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps an input");
 
   vtb::AttnParams p = make_params(d);
@@ -227,7 +240,7 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   if (!workspace || workspace_bytes < need)
     return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
 
-  if (!P && vtb::decode_applicable(p)) {
+  if (!P && vtb::decode_applicable(p)) {   // a saved O is not read: D comes from the chunk statistics
     p.lse = lse;
     return hip_status(vtb::launch_decode(p, workspace, s, ev.pass(0), ev.pass(1)), "decode path");
   }
@@ -237,6 +250,11 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
   int mode;
   if (P) {
     mode = vtb::ROW_P_GIVEN;
+  } else if (o) {
+    p.lse = lse;
+    p.o = o;
+    for (int i = 0; i < 3; ++i) p.so[i] = so[i];
+    mode = vtb::ROW_D_GIVEN;
   } else if (lse) {
     p.lse = lse;
     mode = vtb::ROW_LSE_GIVEN;
@@ -246,8 +264,8 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
     mode = vtb::ROW_LSE_COMPUTE;
   }
   const bool mfma = vtb::mfma_path_applicable(p);
-  if (mfma && mode == vtb::ROW_LSE_GIVEN)
-    rc = hip_status(vtb::launch_mfma_dq(p, s, ev.pass(0)), "dq pass");
+  if (mfma && (mode == vtb::ROW_LSE_GIVEN || mode == vtb::ROW_D_GIVEN))
+    rc = hip_status(vtb::launch_mfma_dq(p, s, ev.pass(0), mode == vtb::ROW_D_GIVEN), "dq pass");
   else
     rc = hip_status(vtb::launch_flash_dq(p, mode, s, ev.pass(0)), "flash dq pass");
   if (rc) return rc;
@@ -264,6 +282,14 @@ int attn_bwd(const attn_bwd_desc* d, const void* q, const void* k, const void* v
              const float* P, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, vtb_stream_t stream) {
   return attn_bwd_impl(d, q, k, v, dout, lse, P, dq, dk, dv, workspace, workspace_bytes,
                        reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0});
+}
+
+int attn_bwd_o(const attn_bwd_desc* d, const void* q, const void* k, const void* v, const void* dout, const void* o,
+               const int64_t* s_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, vtb_stream_t stream) {
+  if (!o) return fail(VTB_ERR_ARG, "o is NULL (use attn_bwd without a saved O)");
+  return attn_bwd_impl(d, q, k, v, dout, lse, nullptr, dq, dk, dv, workspace, workspace_bytes,
+                       reinterpret_cast<hipStream_t>(stream), PhaseEvents{nullptr, 0}, o, s_o);
 }
 
 }  // extern "C"

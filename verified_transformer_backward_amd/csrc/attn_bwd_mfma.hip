@@ -172,6 +172,9 @@ __device__ __forceinline__ void store4(void* base, int bf16, int64_t off, float 
 // starting at qw0. Per 64-key block the wave computes S^T = K Q^T and dP^T = V dO^T
 // (keys as MFMA rows, so a lane owns one query column and its row sums stay in the
 // lane), then A^T += K^T (P o dP)^T and B^T += K^T P^T with K^T from LDS transpose reads.
+// DG (the forward's saved O given): D = dO . O from the rows loaded below, written to dlt
+// for the dk/dv pass; the sweep accumulates A^T += K^T (P o (dP - D))^T only and dQ = scale A.
+template <bool DG>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void dq_mfma_kernel(AttnParams p) {
   constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
@@ -194,7 +197,7 @@ void dq_mfma_kernel(AttnParams p) {
 
   // Q and dO of the lane's queries: B operands (k = d, n = query) of S^T and dP^T.
   bf16x8 qa[kNT][kNKS], da[kNT][kNKS];
-  float lse2[kNT];
+  float lse2[kNT], dg[kNT];
 #pragma unroll
   for (int qt = 0; qt < kNT; ++qt) {
     const int i = min(qw0 + 16 * qt + lc, Tq - 1);
@@ -204,6 +207,19 @@ void dq_mfma_kernel(AttnParams p) {
       da[qt][ks] = load8<__bf16>(Oh + (int64_t)i * p.sdo[1] + 32 * ks + 8 * lg);
     }
     lse2[qt] = p.lse[rowbase + i] * kLog2e;
+    dg[qt] = 0.f;
+    if constexpr (DG) {
+      const __bf16* Oo = reinterpret_cast<const __bf16*>(p.o) + (int64_t)b * p.so[0] + (int64_t)i * p.so[1] +
+                         (int64_t)h * p.so[2];
+#pragma unroll
+      for (int ks = 0; ks < kNKS; ++ks) {
+        const bf16x8 o8 = load8<__bf16>(Oo + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dg[qt] = fmaf((float)da[qt][ks][e], (float)o8[e], dg[qt]);
+      }
+      dg[qt] += __shfl_xor(dg[qt], 16, 64);   // the four 16-lane groups hold the row's pieces
+      dg[qt] += __shfl_xor(dg[qt], 32, 64);
+    }
   }
 
   f32x4 acA[kNDT][kNT], acB[kNDT][kNT];
@@ -309,7 +325,7 @@ void dq_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float pr = pe[kt][qt][r];
-          const float x = pr * dT[kt][qt][r];
+          const float x = DG ? pr * (dT[kt][qt][r] - dg[qt]) : pr * dT[kt][qt][r];
           const __bf16 xr = (__bf16)x;
           dsum[qt] += x;
           dsum_r[qt] += (float)xr;
@@ -328,7 +344,7 @@ void dq_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int qt = 0; qt < kNT; ++qt) {
         mma(acA[dt][qt], kT[pr % (AHEAD + 1)], xb[c][qt]);
-        mma(acB[dt][qt], kT[pr % (AHEAD + 1)], pb[c][qt]);
+        if constexpr (!DG) mma(acB[dt][qt], kT[pr % (AHEAD + 1)], pb[c][qt]);
       }
       fence();
     }
@@ -371,9 +387,9 @@ void dq_mfma_kernel(AttnParams p) {
     d += __shfl_xor(d, 32, 64);
     dr += __shfl_xor(dr, 16, 64);
     dr += __shfl_xor(dr, 32, 64);
-    Dq[qt] = dr;
+    Dq[qt] = DG ? 0.f : dr;   // with D from O, A already holds (P o (dP - D)) K
     const int i = qw0 + 16 * qt + lc;
-    if (lg == 0 && i < Tq) p.dlt[rowbase + i] = d;
+    if (lg == 0 && i < Tq) p.dlt[rowbase + i] = DG ? dg[qt] : d;
   }
   // dQ = scale (A - D B): the lane holds d = 16 dt + 4 lg + r of query qw0 + 16 qt + lc.
 #pragma unroll
@@ -868,10 +884,13 @@ hipError_t launch_mfma_fwd(const AttnParams& p, hipStream_t s, KernelEvents ev) 
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev) {
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev, bool d_given) {
   constexpr int BM = kW * 16 * kNT;
   const dim3 grid(p.B * p.Hq, (p.Tq + BM - 1) / BM);
-  launch_kernel(dq_mfma_kernel, grid, dim3(kT), 0, s, ev, p);
+  if (d_given)
+    launch_kernel(dq_mfma_kernel<true>, grid, dim3(kT), 0, s, ev, p);
+  else
+    launch_kernel(dq_mfma_kernel<false>, grid, dim3(kT), 0, s, ev, p);
   return hipGetLastError();
 }
 

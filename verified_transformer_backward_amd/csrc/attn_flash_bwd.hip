@@ -117,7 +117,7 @@ void flash_dq_kernel(AttnParams p) {
     if constexpr (kNeedS) qa[ks] = load8<E>(row_ptr<E>(p.q, p.sq, b, qc, h) + 32 * ks + 8 * lg);
     if constexpr (kNeedDP) da[ks] = load8<E>(row_ptr<E>(p.dout, p.sdo, b, qc, h) + 32 * ks + 8 * lg);
   }
-  float lrow = MODE == ROW_LSE_GIVEN ? p.lse[rowbase + qc] * kLog2e : 0.f;   // log2-domain lse
+  float lrow = (MODE == ROW_LSE_GIVEN || MODE == ROW_D_GIVEN) ? p.lse[rowbase + qc] * kLog2e : 0.f;   // log2 domain
 
   const int last_row = min(Tq, (qb + 1) * BM) - 1;
   const int kend = p.causal ? min(Tk, last_row + off + 1) : Tk;
@@ -260,10 +260,10 @@ void flash_dq_kernel(AttnParams p) {
     }
   };
 
-  // ---- sweep 1: row term D (and lse)
+  // ---- sweep 1: row term D (and lse); with D given, none
   float accd = 0.f, mrun = -INFINITY, lrun = 0.f, urun = 0.f;
-  start_sweep();
-  for (int jb = 0; jb < kend; jb += BN) {
+  if constexpr (MODE != ROW_D_GIVEN) start_sweep();
+  for (int jb = 0; MODE != ROW_D_GIVEN && jb < kend; jb += BN) {
     stage_block(jb);
     f32x4 sT[4], dpT[4];
     block_scores(sT, dpT);
@@ -300,6 +300,18 @@ void flash_dq_kernel(AttnParams p) {
     lrow = M + log2f(Ls);
     drow = U / Ls;
     if (lg == 0 && qok) p.lse_out[rowbase + qrow] = lrow * kLn2;
+  } else if constexpr (MODE == ROW_D_GIVEN) {
+    // D = dO . O: the lane's dO pieces (d = 32 ks + 8 lg + e) against the same pieces of O,
+    // then the four 16-lane groups that hold the row
+    drow = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const frag_t<E> o8 = load8<E>(row_ptr<E>(p.o, p.so, b, qc, h) + 32 * ks + 8 * lg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) drow = fmaf(to_f32(da[ks][e]), to_f32(o8[e]), drow);
+    }
+    drow += __shfl_xor(drow, 16, 64);
+    drow += __shfl_xor(drow, 32, 64);
   } else {
     drow = accd + __shfl_xor(accd, 16, 64);
     drow += __shfl_xor(drow, 32, 64);
@@ -539,6 +551,7 @@ hipError_t dq_dispatch(const AttnParams& p, int mode, hipStream_t s, KernelEvent
     case ROW_LSE_COMPUTE: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_COMPUTE>, grid, dim3(kThreads), 0, s, ev, p); break;
     case ROW_LSE_ONLY: launch_kernel(flash_dq_kernel<E, D, ROW_LSE_ONLY>, grid, dim3(kThreads), 0, s, ev, p); break;
     case ROW_FWD: launch_kernel(flash_dq_kernel<E, D, ROW_FWD>, grid, dim3(kThreads), 0, s, ev, p); break;
+    case ROW_D_GIVEN: launch_kernel(flash_dq_kernel<E, D, ROW_D_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
     default: launch_kernel(flash_dq_kernel<E, D, ROW_P_GIVEN>, grid, dim3(kThreads), 0, s, ev, p); break;
   }
   return hipGetLastError();

@@ -17,6 +17,7 @@ struct AttnParams {
   const void* dout;
   const float* lse;   // row log-sum-exp read by the backward (given or workspace)
   const float* P;     // saved softmax [B, Hq, Tq, Tk] or nullptr
+  const void* o;      // the forward's saved output [B, Tq, Hq, D] (ROW_D_GIVEN), strides so
   float* lse_out;     // where a pass that computes lse writes it
   float* dlt;         // workspace [B, Hq, Tq]: D_i = rowsum(P o dP)
   void* dq;
@@ -26,7 +27,7 @@ struct AttnParams {
   float scale;
   int causal;
   int in_bf16, out_bf16;
-  int64_t sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
+  int64_t sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3], so[3];
 };
 
 // Optional timing of one kernel: HIP events that the dispatch itself records at the
@@ -48,7 +49,10 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 // (online max/sum), lse only (no backward), or from a saved softmax P. ROW_FWD is the
 // forward: O = softmax(scale Q K^T) V by online softmax, written through dq / sdq, and
 // lse written to lse_out when that is not null.
-enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3, ROW_FWD = 4 };
+// ROW_D_GIVEN takes the given lse and the forward's saved output o: the row term is
+// D_i = dO_i . O_i (fp32 sum of in-dtype products, formed from the rows the pass loads
+// anyway and written to dlt), then one sweep forms dQ.
+enum RowMode { ROW_LSE_GIVEN = 0, ROW_LSE_COMPUTE = 1, ROW_LSE_ONLY = 2, ROW_P_GIVEN = 3, ROW_FWD = 4, ROW_D_GIVEN = 5 };
 
 // Flash-style path (any Tq): query-parallel pass (row term D, lse when computed, dQ),
 // then key-parallel pass (dK, dV). The second reads D (and lse) written by the first.
@@ -62,7 +66,9 @@ bool mfma_path_applicable(const AttnParams& p);
 // MFMA forward (bf16, D = 128): O and lse by online softmax, O written through dq / sdq.
 bool mfma_fwd_applicable(const AttnParams& p);
 hipError_t launch_mfma_fwd(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
-hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
+// d_given: D = dO . O from the saved output o (written to dlt) and dQ = scale (P o (dP - D)) K
+// takes three contractions per key block instead of four.
+hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev = {}, bool d_given = false);
 hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev = {});
 
 // Decode path (Hq/Hkv * Tq <= 16): a chunk pass (scores, dP, split-KV statistics, dQ
