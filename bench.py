@@ -153,7 +153,7 @@ def graph_ms(torch, hip, fn, reps):
 
 
 EXTRA_NAMES = ("single_query", "decode_gqa", "decode_fwd", "long_causal", "causal_train_f32out", "causal_train_saved_o", "rope_rmsnorm_res", "rope_bwd",
-               "rmsnorm_bwd", "layer_chain", "attn_fwd", "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd")
+               "rmsnorm_bwd", "layer_chain", "attn_fwd", "layernorm_bwd", "relu2_mul_bwd", "ffn_bwd", "attn_block_bwd", "rms_attn_block_bwd")
 
 
 def copy_bandwidth(torch, hip):
@@ -512,6 +512,51 @@ def extra_workloads(torch, vtb, hip, only=None):
                                               "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
                                               "algorithmic_flops": fl}}
         del saved, xin, wqkv, wo, dx2, ln_y, qkv, P, ctx, dx, dwq, dwo, bws
+
+    if want("rms_attn_block_bwd"):
+        # one Hesper-form attention layer's backward (RMSNorm with gain, QKV projection, RoPE
+        # on q and k, causal attention with the saved softmax, output projection), T256
+        # 20 x 128 fp32; saved activations from a torch fp32 forward (setup only)
+        Tb, Hb, db = 256, 20, 128
+        Cb = Hb * db
+        sc = 1.0 / np.sqrt(db)
+        p = synth.rms_block_inputs(1, Tb, Hb, db)
+        x, gam, wqkv, wo, dx2 = (up(p[n]) for n in ("x", "gamma", "w_qkv", "w_o", "dx2"))
+        n_ = (gam * x / torch.sqrt((x * x).mean(1, keepdim=True) + 1e-6)).contiguous()
+        abv = n_ @ wqkv
+        th = torch.arange(Tb, device=dev, dtype=torch.float64)[:, None] * \
+            10000.0 ** (-2.0 * torch.arange(db // 2, device=dev, dtype=torch.float64)[None, :] / db)
+        cs, sn = torch.cos(th).float()[:, None, :], torch.sin(th).float()[:, None, :]
+
+        def rot(z):
+            z = z.reshape(Tb, Hb, db // 2, 2)
+            return torch.stack([z[..., 0] * cs - z[..., 1] * sn, z[..., 0] * sn + z[..., 1] * cs], -1).reshape(Tb, Cb)
+
+        qkv = torch.cat([rot(abv[:, :Cb]), rot(abv[:, Cb:2 * Cb]), abv[:, 2 * Cb:]], 1).contiguous()
+        hsplit = lambda z: z.reshape(Tb, Hb, db).permute(1, 0, 2).contiguous()
+        q, k, v = hsplit(qkv[:, :Cb]), hsplit(qkv[:, Cb:2 * Cb]), hsplit(qkv[:, 2 * Cb:])
+        mask = torch.tril(torch.ones(Tb, Tb, dtype=torch.bool, device=dev))
+        P = torch.softmax((torch.matmul(q, k.transpose(1, 2).contiguous()) * sc).masked_fill(~mask, float("-inf")),
+                          -1).contiguous()
+        ctx = torch.matmul(P, v).permute(1, 0, 2).reshape(Tb, Cb).contiguous()
+        saved = {"x": x, "gamma": gam, "n": n_, "w_qkv": wqkv, "qkv": qkv, "P": P, "ctx": ctx, "w_o": wo}
+        outs = dict(dx=torch.empty_like(dx2), dgamma=torch.empty_like(gam), dw_qkv=torch.empty_like(wqkv),
+                    dw_o=torch.empty_like(wo))
+        rws = torch.empty(vtb.rms_attn_block_bwd_workspace_size(vtb.make_rms_block_cfg(1, Tb, Hb, db, sc)),
+                          dtype=torch.uint8, device=dev)
+        f = lambda: vtb.rms_attn_block_bwd(saved, dx2, 1, Hb, sc, True, workspace=rws, stream=torch.cuda.current_stream(),
+                                           **outs)
+        ms = graph_ms(torch, hip, f, 10)
+        pairs = Hb * Tb * (Tb + 1) // 2
+        fl = 4 * Tb * Cb * Cb + 4 * Tb * Cb * 3 * Cb + 8 * db * pairs   # Wo, Wqkv products; 4 attention contractions
+        out["rms_attn_block_bwd"] = {"workload": "Hesper-form attention layer backward (RMSNorm with gain, QKV "
+                                                 "projection, RoPE on q and k, saved-softmax causal attention, output "
+                                                 "projection), T256 20 x 128 fp32",
+                                     "ms": round(ms, 4), "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                                     "roofline": {"bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
+                                                  "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                                                  "algorithmic_flops": fl}}
+        del saved, outs, rws, x, gam, wqkv, wo, dx2, n_, abv, qkv, P, ctx
 
     if want("layer_chain"):
         # 30-layer chain: T256, hidden 2560 = 20 x 128, fp32, saved softmax P per layer

@@ -346,6 +346,52 @@ size_t attn_block_bwd_workspace_size(const attn_block_cfg* cfg);
 int attn_block_bwd(const attn_block_cfg* cfg, const attn_block_saved* saved, const float* dx2, float* dx,
                    float* dw_qkv, float* dw_o, void* workspace, size_t workspace_bytes, vtb_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * One attention layer of the Hesper form, backward: RMSNorm with a learned gain, Q/K/V
+ * projections, RoPE on the projected queries and keys, causal attention, output projection
+ * and residual. The pieces are "Hesper.Training.VerifiedBackward"'s rmsNormForward /
+ * rmsNormBackward (section "RMSNorm"), ropeForward / ropeBackward (section "RoPE (Rotary
+ * Position Embedding)") and its attention chain (section "Attention (full single-head)"),
+ * with the causal mask and the fused Q/K/V weight gradient of the DaisyChain-Train
+ * transformer.js `backward`. Over B sequences of T tokens, hidden C = H * D, positions
+ * t = 0 .. T-1 within each sequence, the forward
+ *     n = gamma o x / r_t (r_t = sqrt(mean(x_t^2) + eps)),  [a | b | v] = n Wqkv,
+ *     q = RoPE(a), k = RoPE(b) per head,  P = causal softmax(scale q_h k_h^T),
+ *     ctx = P v_h,  x2 = x + ctx Wo
+ * has the backward from dx2
+ *     gWo, dctx  = ctx^T dx2, dx2 Wo^T
+ *     dq, dk, dv = attention backward with the saved P
+ *     da, db     = RoPEBackward(dq), RoPEBackward(dk)          (rotation by -theta)
+ *     gWqkv, dn  = n^T [da | db | dv], [da | db | dv] Wqkv^T
+ *     dx         = dx2 + RMSNormBackward(x, gamma, dn),  dgamma = sum_t dn_t o x_t / r_t
+ * (dgamma: the derivative of the same RMSNorm map in gamma). RoPE angles are
+ * t * rope_base^(-2i / D); rope_layout 0 pairs (2i, 2i+1), 1 pairs (i, i + D/2).
+ * Saved tensors (fp32, row-major, 16-byte aligned): x [B T, C], gamma [C], n [B T, C] (the
+ * RMSNorm output), w_qkv [C, 3C], qkv [B T, 3C] (the rotated q and k, then v; head h at
+ * columns h D of each third), P [B H, T, T], ctx [B T, C], w_o [C, C]. Outputs: dx [B T, C],
+ * dgamma [C], dw_qkv [C, 3C], dw_o [C, C]. dx == dx2 is allowed; no other overlap. Every
+ * reduction runs in a fixed order: results are bitwise reproducible. Workspace from
+ * rms_attn_block_bwd_workspace_size().
+ * -------------------------------------------------------------------------------------*/
+typedef struct {
+  int32_t B, T, H, D;
+  float scale;
+  int32_t causal;
+  float eps;
+  double rope_base;
+  int32_t rope_layout;
+} rms_attn_block_cfg;
+
+typedef struct {
+  const float *x, *gamma, *n, *w_qkv, *qkv, *P, *ctx, *w_o;
+} rms_attn_block_saved;
+
+size_t rms_attn_block_bwd_workspace_size(const rms_attn_block_cfg* cfg);
+
+int rms_attn_block_bwd(const rms_attn_block_cfg* cfg, const rms_attn_block_saved* saved, const float* dx2,
+                       float* dx, float* dgamma, float* dw_qkv, float* dw_o, void* workspace,
+                       size_t workspace_bytes, vtb_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,4 +29,5 @@ from .gen import (  # noqa: F401
     relu2_inputs,
     ffn_inputs,
     block_inputs,
+    rms_block_inputs,
 )

@@ -200,3 +200,16 @@ def block_inputs(B: int = 1, T: int = 256, H: int = 20, d: int = 128, seed: int 
     w_o = normal(rng, (C, C), std=0.02)
     dx2 = normal(rng, (B * T, C))
     return dict(xin=xin, w_qkv=w_qkv, w_o=w_o, dx2=dx2)
+
+
+def rms_block_inputs(B: int = 1, T: int = 256, H: int = 20, d: int = 128, seed: int = 1010, w_std: float = 0.02):
+    """One Hesper-form attention layer's input and parameters: x, dx2 N(0, 1); gamma
+    U(0.5, 1.5); Wqkv [C, 3C] and Wo [C, C] N(0, w_std). fp32."""
+    rng = np.random.default_rng(seed)
+    C = H * d
+    x = normal(rng, (B * T, C))
+    gamma = uniform(rng, (C,), 0.5, 1.5)
+    w_qkv = normal(rng, (C, 3 * C), std=w_std)
+    w_o = normal(rng, (C, C), std=w_std)
+    dx2 = normal(rng, (B * T, C))
+    return dict(x=x, gamma=gamma, w_qkv=w_qkv, w_o=w_o, dx2=dx2)

@@ -207,6 +207,27 @@ def test_attn_block_validation_codes():
     assert ok(c=bad) == 1
 
 
+def test_rms_attn_block_validation_codes():
+    L = vtb.lib()
+    cfg = vtb.make_rms_block_cfg(1, 8, 2, 8, 0.35)
+    sv = vtb.RmsAttnBlockSaved(*[A0 + i * 0x1000000 for i in range(8)])
+    need = L.rms_attn_block_bwd_workspace_size(ctypes.byref(cfg))
+    assert need > 0
+
+    def call(c=cfg, s=sv, dx2=A1 + 0x9000000, dx=A2, dg=A3, dq=A4, do=A5, ws=WS, wsb=need):
+        return L.rms_attn_block_bwd(ctypes.byref(c), ctypes.byref(s), dx2, dx, dg, dq, do, ws, wsb, None)
+
+    assert L.rms_attn_block_bwd(None, ctypes.byref(sv), A1, A2, A3, A4, A5, WS, need, None) == 1
+    assert call(c=vtb.make_rms_block_cfg(1, 8, 2, 7, 0.35)) == 1            # odd head dim
+    assert call(c=vtb.make_rms_block_cfg(1, 8, 2, 8, 0.35, eps=0.0)) == 1    # eps must be positive
+    assert call(c=vtb.make_rms_block_cfg(1, 8, 2, 8, 0.35, rope_layout=2)) == 1
+    assert call(dg=None) == 1
+    assert call(dg=A3 + 4) == 2                                             # unaligned
+    assert call(dx=A0) == 3                                                 # dx over the saved x
+    assert call(dq=A2) == 3                                                 # two outputs on one buffer
+    assert call(wsb=need - 256) == 4
+
+
 def test_bf16_elementwise_entry_points_validate():
     L = vtb.lib()
     assert L.rope_bwd_ex(5, A0, A1, 4, 2, 8, 16, None, 0, 10000.0, 0, None) == 1        # dtype

@@ -31,7 +31,7 @@ EXPORTS = (
     "rope_bwd", "rmsnorm_bwd", "rope_bwd_ex", "rmsnorm_bwd_ex", "rope_rmsnorm_res_bwd", "linear_bwd", "layernorm_bwd",
     "relu2_mul_bwd",
     "layer_bwd_workspace_size", "layer_bwd", "ffn_bwd_workspace_size", "ffn_bwd",
-    "attn_block_bwd_workspace_size", "attn_block_bwd",
+    "attn_block_bwd_workspace_size", "attn_block_bwd", "rms_attn_block_bwd_workspace_size", "rms_attn_block_bwd",
 )
 
 
@@ -79,6 +79,19 @@ BLOCK_SAVED = ("ln_y", "ln_sig", "w_qkv", "qkv", "P", "ctx", "w_o")
 
 class AttnBlockSaved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_SAVED]
+
+
+class RmsAttnBlockCfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_base", ctypes.c_double), ("rope_layout", ctypes.c_int32)]
+
+
+RMS_BLOCK_SAVED = ("x", "gamma", "n", "w_qkv", "qkv", "P", "ctx", "w_o")
+
+
+class RmsAttnBlockSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in RMS_BLOCK_SAVED]
 
 
 FFN_SAVED = ("x", "gamma1", "xn", "w_gu", "gu", "gamma2", "hn", "w_down")
@@ -129,6 +142,9 @@ def lib() -> ctypes.CDLL:
         "ffn_bwd_workspace_size": (SZ, [ctypes.POINTER(FfnBwdCfg)]),
         "ffn_bwd": (ctypes.c_int, [ctypes.POINTER(FfnBwdCfg), ctypes.POINTER(FfnSaved), P, P, P, P, P, SZ, P]),
         "attn_block_bwd_workspace_size": (SZ, [ctypes.POINTER(AttnBlockCfg)]),
+        "rms_attn_block_bwd_workspace_size": (SZ, [ctypes.POINTER(RmsAttnBlockCfg)]),
+        "rms_attn_block_bwd": (ctypes.c_int, [ctypes.POINTER(RmsAttnBlockCfg), ctypes.POINTER(RmsAttnBlockSaved), P, P, P,
+                                              P, P, P, SZ, P]),
         "attn_block_bwd": (ctypes.c_int, [ctypes.POINTER(AttnBlockCfg), ctypes.POINTER(AttnBlockSaved), P, P, P, P, P, SZ,
                                           P]),
     }
@@ -589,3 +605,50 @@ def attn_block_bwd(saved: dict, dx2, B: int, H: int, scale: float, causal: bool 
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_block_bwd")
     return dx, dw_qkv, dw_o
+
+
+def make_rms_block_cfg(B, T, H, D, scale, causal=True, eps=1e-6, rope_base=10000.0, rope_layout=0) -> RmsAttnBlockCfg:
+    c = RmsAttnBlockCfg()
+    c.B, c.T, c.H, c.D, c.scale, c.causal = int(B), int(T), int(H), int(D), float(scale), int(bool(causal))
+    c.eps, c.rope_base, c.rope_layout = float(eps), float(rope_base), int(rope_layout)
+    return c
+
+
+def rms_attn_block_bwd_workspace_size(cfg: RmsAttnBlockCfg) -> int:
+    return int(lib().rms_attn_block_bwd_workspace_size(ctypes.byref(cfg)))
+
+
+def rms_attn_block_bwd(saved: dict, dx2, B: int, H: int, scale: float, causal: bool = True, eps: float = 1e-6,
+                       rope_base: float = 10000.0, rope_layout: int = 0, dx=None, dgamma=None, dw_qkv=None, dw_o=None,
+                       workspace=None, stream=None):
+    """Backward of one Hesper-form attention layer over its saved tensors (x, gamma, n,
+    w_qkv, qkv, P, ctx, w_o; fp32 contiguous); dx2 is [B T, C]. Returns (dx, dgamma,
+    dw_qkv, dw_o)."""
+    for n in RMS_BLOCK_SAVED:
+        t = saved[n]
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"saved[{n!r}] must be contiguous float32")
+        _same_device(t, dx2, f"saved[{n!r}]")
+    if dx2.dtype != torch.float32 or not dx2.is_contiguous() or dx2.dim() != 2:
+        raise TypeError("dx2 must be a contiguous float32 [B T, C] tensor")
+    BT, C = dx2.shape
+    if BT % B or C % H:
+        raise ValueError("dx2 rows must be B * T and its width H * D")
+    T = BT // B
+    want = {"x": (BT, C), "gamma": (C,), "n": (BT, C), "w_qkv": (C, 3 * C), "qkv": (BT, 3 * C), "P": (B * H, T, T),
+            "ctx": (BT, C), "w_o": (C, C)}
+    for n, shp in want.items():
+        if tuple(saved[n].shape) != shp:
+            raise ValueError(f"saved[{n!r}] has shape {tuple(saved[n].shape)}, expected {shp}")
+    cfg = make_rms_block_cfg(B, T, H, C // H, scale, causal, eps, rope_base, rope_layout)
+    sv = RmsAttnBlockSaved(*[saved[n].data_ptr() for n in RMS_BLOCK_SAVED])
+    dx = _out(dx, (BT, C), "dx", dx2.device)
+    dgamma = _out(dgamma, (C,), "dgamma", dx2.device)
+    dw_qkv = _out(dw_qkv, (C, 3 * C), "dw_qkv", dx2.device)
+    dw_o = _out(dw_o, (C, C), "dw_o", dx2.device)
+    if workspace is None:
+        workspace = _workspace(rms_attn_block_bwd_workspace_size(cfg), dx2.device)
+    _check(lib().rms_attn_block_bwd(ctypes.byref(cfg), ctypes.byref(sv), _ptr(dx2), _ptr(dx), _ptr(dgamma), _ptr(dw_qkv),
+                                    _ptr(dw_o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "rms_attn_block_bwd")
+    return dx, dgamma, dw_qkv, dw_o

@@ -794,4 +794,110 @@ int attn_block_bwd(const attn_block_cfg* c, const attn_block_saved* sv, const fl
   return hip_status(vtb::launch_layernorm_bwd(0, dln, sv->ln_y, sv->ln_sig, dx2, dx, bt, ci, s), "block layernorm");
 }
 
+
+size_t rms_attn_block_bwd_workspace_size(const rms_attn_block_cfg* c) {
+  if (!c || c->B < 1 || c->T < 1 || c->H < 1 || c->D < 2) return 0;
+  const size_t BT = (size_t)c->B * c->T, C = (size_t)c->H * c->D, T = c->T;
+  const int bt = c->B * c->T, ci = c->H * c->D;
+  // dctx [BT, C], dn [BT, C], dS [H, T, T], dqkv [BT, 3C], 1/r [BT], dX partials of either split product
+  const size_t parts = std::max((size_t)vtb::linear_bwd_splits(bt, ci, ci), (size_t)vtb::linear_bwd_splits(bt, ci, 3 * ci)) *
+                       BT * C;
+  return align256(BT * C * 4) * 2 + align256((size_t)c->H * T * T * 4) + align256(BT * 3 * C * 4) + align256(BT * 4) +
+         align256(parts * 4);
+}
+
+int rms_attn_block_bwd(const rms_attn_block_cfg* c, const rms_attn_block_saved* sv, const float* dx2, float* dx,
+                       float* dgamma, float* dw_qkv, float* dw_o, void* workspace, size_t workspace_bytes,
+                       vtb_stream_t stream) {
+  g_last_error.clear();
+  if (!c || !sv) return fail(VTB_ERR_ARG, "cfg and saved must be non-NULL");
+  if (c->B < 1 || c->T < 1 || c->H < 1 || c->D < 2 || (c->D & 1))
+    return fail(VTB_ERR_ARG, "B=%d T=%d H=%d D=%d must be >= 1 (D even, >= 2)", c->B, c->T, c->H, c->D);
+  if (!std::isfinite(c->scale)) return fail(VTB_ERR_ARG, "scale is not finite");
+  if (c->causal != 0 && c->causal != 1) return fail(VTB_ERR_ARG, "causal must be 0 or 1");
+  if (!(c->eps > 0.f) || !std::isfinite(c->eps)) return fail(VTB_ERR_ARG, "eps must be positive and finite");
+  if (!(c->rope_base > 0.0) || !std::isfinite(c->rope_base)) return fail(VTB_ERR_ARG, "rope_base must be positive");
+  if (c->rope_layout != 0 && c->rope_layout != 1) return fail(VTB_ERR_ARG, "rope_layout must be 0 or 1");
+  const int64_t BT = (int64_t)c->B * c->T, C = (int64_t)c->H * c->D, T = c->T;
+  if (BT * 3 * C > ((int64_t)1 << 31) || C * 3 * C > ((int64_t)1 << 31) || (int64_t)c->B * c->H * T * T > ((int64_t)1 << 31))
+    return fail(VTB_ERR_UNSUPPORTED, "a tensor exceeds 2^31 elements");
+  const float* in_ptrs[9] = {sv->x, sv->gamma, sv->n, sv->w_qkv, sv->qkv, sv->P, sv->ctx, sv->w_o, dx2};
+  for (const float* ptr : in_ptrs)
+    if (!ptr) return fail(VTB_ERR_ARG, "a saved tensor or dx2 is NULL");
+  if (!dx || !dgamma || !dw_qkv || !dw_o) return fail(VTB_ERR_ARG, "outputs must be non-NULL");
+  for (const float* ptr : in_ptrs)
+    if (!aligned16(ptr)) return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (!aligned16(dx) || !aligned16(dgamma) || !aligned16(dw_qkv) || !aligned16(dw_o) || !aligned16(workspace))
+    return fail(VTB_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const size_t in_bytes[9] = {(size_t)(BT * C * 4), (size_t)(C * 4), (size_t)(BT * C * 4), (size_t)(C * 3 * C * 4),
+                              (size_t)(BT * 3 * C * 4), (size_t)((int64_t)c->B * c->H * T * T * 4), (size_t)(BT * C * 4),
+                              (size_t)(C * C * 4), (size_t)(BT * C * 4)};
+  Span ins[9];
+  for (int i = 0; i < 9; ++i) ins[i] = span_of(in_ptrs[i], in_bytes[i]);
+  const Span sdx = span_of(dx, BT * C * 4), sg = span_of(dgamma, C * 4), sq = span_of(dw_qkv, C * 3 * C * 4),
+             so = span_of(dw_o, C * C * 4);
+  for (int i = 0; i < 9; ++i) {
+    if (i != 8 && overlap(sdx, ins[i])) return fail(VTB_ERR_ALIAS, "dx overlaps saved tensor %d", i);
+    if (overlap(sg, ins[i]) || overlap(sq, ins[i]) || overlap(so, ins[i]))
+      return fail(VTB_ERR_ALIAS, "a parameter gradient overlaps input %d", i);
+  }
+  if (dx != dx2 && overlap(sdx, ins[8])) return fail(VTB_ERR_ALIAS, "dx partially overlaps dx2");
+  const Span outs[4] = {sdx, sg, sq, so};
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return fail(VTB_ERR_ALIAS, "outputs overlap");
+  const size_t need = rms_attn_block_bwd_workspace_size(c);
+  if (!workspace || workspace_bytes < need)
+    return fail(VTB_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+  const Span sws = span_of(workspace, need);
+  for (int i = 0; i < 9; ++i)
+    if (overlap(sws, ins[i])) return fail(VTB_ERR_ALIAS, "workspace overlaps input %d", i);
+  for (int a = 0; a < 4; ++a)
+    if (overlap(sws, outs[a])) return fail(VTB_ERR_ALIAS, "workspace overlaps an output");
+
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int bt = (int)BT, ci = (int)C, H = c->H, D = c->D, Ti = c->T;
+  char* base = reinterpret_cast<char*>(workspace);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    float* ptr = reinterpret_cast<float*>(base + off);
+    off += align256(bytes);
+    return ptr;
+  };
+  float* dctx = carve(BT * C * 4);
+  float* dn = carve(BT * C * 4);
+  float* ds = carve((size_t)H * T * T * 4);
+  float* dqkv = carve(BT * 3 * C * 4);
+  float* rinv = carve(BT * 4);
+  float* part = carve(0);
+
+  // 1. output projection: dctx = dx2 Wo^T, gWo = ctx^T dx2
+  int rc = hip_status(vtb::launch_linear_bwd_split(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, s), "layer Wo");
+  if (rc) return rc;
+  for (int b = 0; b < c->B; ++b) {
+    const int64_t r3 = (int64_t)b * Ti * 3 * C, r1 = (int64_t)b * Ti * C;
+    const float* q = sv->qkv + r3;
+    float* dq = dqkv + r3;
+    // 2. attention backward with the saved softmax into the q | k | v thirds of dqkv
+    rc = hip_status(vtb::launch_attn_saved_p_bwd_ld(q, q + C, q + 2 * C, dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq,
+                                                    dq + C, dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal,
+                                                    s),
+                    "layer attention");
+    if (rc) return rc;
+    // 3. RoPE backward on dq and dk in place: their 2H heads are the first 2C columns of
+    //    each dqkv row, positions 0 .. T-1 of this sequence
+    rc = hip_status(vtb::launch_rope_bwd(0, dq, dq, Ti, 2 * H, D, 3 * C, nullptr, 0, c->rope_base, c->rope_layout, s),
+                    "layer RoPE backward");
+    if (rc) return rc;
+  }
+  // 4. Q/K/V projection as one product: dn = dqkv Wqkv^T, gWqkv = n^T dqkv
+  rc = hip_status(vtb::launch_linear_bwd_split(sv->n, sv->w_qkv, dqkv, dn, dw_qkv, bt, ci, 3 * ci, part, s), "layer Wqkv");
+  if (rc) return rc;
+  // 5. RMSNorm backward plus the residual (dx = dx2 + RMSNormBackward(x, gamma, dn), 1/r kept),
+  //    then the gain gradient dgamma = sum_t dn_t o x_t / r_t
+  rc = hip_status(vtb::launch_rmsnorm_res_bwd(sv->x, sv->gamma, dn, dx2, dx, bt, ci, c->eps, s, rinv), "layer RMSNorm");
+  if (rc) return rc;
+  return hip_status(vtb::launch_rmsnorm_gamma(sv->x, dn, rinv, dgamma, bt, ci, s), "layer RMSNorm gain");
+}
+
 }  // extern "C"

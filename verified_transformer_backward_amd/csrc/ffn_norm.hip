@@ -281,13 +281,14 @@ __global__ __launch_bounds__(256) void subnorm_relu2_bwd_any_kernel(const float*
 }
 
 // RMSNorm backward plus the residual, one 256-thread block per row of n values:
-//     dx = dres + RMSNormBackward(x, gamma, dy).
+//     dx = dres + RMSNormBackward(x, gamma, dy),
+// and, when rinv is not null, the row's 1 / r in rinv[row] (for the gain gradient).
 // dx == dres is allowed: each element of dres is read before the same thread writes it.
 template <int NV>
 __global__ __launch_bounds__(256) void rmsnorm_res_bwd_vec_kernel(const f32x4* __restrict__ x,
                                                                   const f32x4* __restrict__ gamma,
                                                                   const f32x4* __restrict__ dy, const f32x4* dres,
-                                                                  f32x4* dx, int n, float eps) {
+                                                                  f32x4* dx, int n, float eps, float* rinv_out) {
   const int64_t t = blockIdx.x;
   const int n4 = n / 4;
   f32x4 xv[NV], gy[NV], rv[NV];
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(256) void rmsnorm_res_bwd_vec_kernel(const f32x4* _
   const float r2 = tot.x / n + eps;
   const float rinv = rsqrtf(r2);
   const float coef = tot.y / (n * r2);
+  if (rinv_out && threadIdx.x == 0) rinv_out[t] = rinv;
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
     const int c = (int)threadIdx.x + 256 * e;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(256) void rmsnorm_res_bwd_vec_kernel(const f32x4* _
 __global__ __launch_bounds__(256) void rmsnorm_res_bwd_any_kernel(const float* __restrict__ x,
                                                                   const float* __restrict__ gamma,
                                                                   const float* __restrict__ dy, const float* dres,
-                                                                  float* dx, int n, float eps) {
+                                                                  float* dx, int n, float eps, float* rinv_out) {
   const int64_t t = blockIdx.x;
   const float* xr = x + t * n;
   const float* dyr = dy + t * n;
@@ -341,7 +343,42 @@ __global__ __launch_bounds__(256) void rmsnorm_res_bwd_any_kernel(const float* _
   const float r2 = tot.x / n + eps;
   const float rinv = rsqrtf(r2);
   const float coef = tot.y / (n * r2);
+  if (rinv_out && threadIdx.x == 0) rinv_out[t] = rinv;
   for (int j = threadIdx.x; j < n; j += 256) dx[t * n + j] = dres[t * n + j] + (dyr[j] * gamma[j] - xr[j] * coef) * rinv;
+}
+
+// RMSNorm gain gradient over rows of n values: dgamma_c = sum_t dy_tc x_tc rinv_t. One
+// 1024-thread block per 64 columns: lane = column, wave w sums rows w, w + 16, ... in
+// order, then the 16 wave partials are added in wave order (bitwise reproducible).
+__global__ __launch_bounds__(1024) void rmsnorm_gamma_kernel(const float* __restrict__ x, const float* __restrict__ dy,
+                                                             const float* __restrict__ rinv, float* dgamma, int rows,
+                                                             int n) {
+  __shared__ float part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int cc = min(c, n - 1);
+  float acc = 0.f;
+  int t = w;
+  for (; t + 48 < rows; t += 64) {   // four rows' loads in flight
+    float xv[4], dv[4], rv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xv[u] = x[(int64_t)(t + 16 * u) * n + cc];
+      dv[u] = dy[(int64_t)(t + 16 * u) * n + cc];
+      rv[u] = rinv[t + 16 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = fmaf(dv[u] * xv[u], rv[u], acc);
+  }
+  for (; t < rows; t += 16) acc = fmaf(dy[(int64_t)t * n + cc] * x[(int64_t)t * n + cc], rinv[t], acc);
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && c < n) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i][lane];
+    dgamma[c] = s;
+  }
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -408,7 +445,7 @@ hipError_t launch_subnorm_relu2_bwd(const float* gu, const float* dhn, const flo
 }
 
 hipError_t launch_rmsnorm_res_bwd(const float* x, const float* gamma, const float* dy, const float* dres, float* dx, int T,
-                           int n, float eps, hipStream_t s) {
+                           int n, float eps, hipStream_t s, float* rinv) {
   const int n4 = n / 4;
   const bool vec = n % 4 == 0 && n4 <= 256 * 4 && al16(x) && al16(gamma) && al16(dy) && al16(dres) && al16(dx);
   if (vec) {
@@ -416,15 +453,21 @@ hipError_t launch_rmsnorm_res_bwd(const float* x, const float* gamma, const floa
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(T), dim3(256), 0, s, reinterpret_cast<const f32x4*>(x),
                          reinterpret_cast<const f32x4*>(gamma), reinterpret_cast<const f32x4*>(dy),
-                         reinterpret_cast<const f32x4*>(dres), reinterpret_cast<f32x4*>(dx), n, eps);
+                         reinterpret_cast<const f32x4*>(dres), reinterpret_cast<f32x4*>(dx), n, eps, rinv);
     };
     if (nv <= 1) go(rmsnorm_res_bwd_vec_kernel<1>);
     else if (nv <= 2) go(rmsnorm_res_bwd_vec_kernel<2>);
     else if (nv <= 3) go(rmsnorm_res_bwd_vec_kernel<3>);
     else go(rmsnorm_res_bwd_vec_kernel<4>);
   } else {
-    hipLaunchKernelGGL(rmsnorm_res_bwd_any_kernel, dim3(T), dim3(256), 0, s, x, gamma, dy, dres, dx, n, eps);
+    hipLaunchKernelGGL(rmsnorm_res_bwd_any_kernel, dim3(T), dim3(256), 0, s, x, gamma, dy, dres, dx, n, eps, rinv);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_gamma(const float* x, const float* dy, const float* rinv, float* dgamma, int rows, int n,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_gamma_kernel, dim3((n + 63) / 64), dim3(1024), 0, s, x, dy, rinv, dgamma, rows, n);
   return hipGetLastError();
 }
 

@@ -119,7 +119,11 @@ hipError_t launch_relu2_mul_bwd(int bf16, const void* gate, const void* up, cons
 hipError_t launch_subnorm_relu2_bwd(const float* gu, const float* dhn, const float* gamma2, float* dgu, int T, int F,
                                     float eps, hipStream_t s);
 hipError_t launch_rmsnorm_res_bwd(const float* x, const float* gamma, const float* dy, const float* dres, float* dx,
-                                  int T, int n, float eps, hipStream_t s);
+                                  int T, int n, float eps, hipStream_t s, float* rinv = nullptr);
+// RMSNorm gain gradient: dgamma[c] = sum_t dy[t, c] x[t, c] rinv[t] over rows t (rinv from
+// launch_rmsnorm_res_bwd), summed in a fixed order.
+hipError_t launch_rmsnorm_gamma(const float* x, const float* dy, const float* rinv, float* dgamma, int rows, int n,
+                                hipStream_t s);
 
 // fp32 MFMA GEMMs of the linear backward (one launch computes both products).
 hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, float* dx, float* dw,
