@@ -58,6 +58,29 @@ constexpr int kWavesPerEU = kNT == 1 ? 2 : 1;   // register budget: 256 or 512 p
 // are unrolled by two so that every LDS address is a per-lane base plus a constant.
 template <int B>
 using BufC = std::integral_constant<int, B>;
+
+// Which (row, rank) a workgroup works on. Rows are gridDim.x (batch x head), ranks are the
+// gridDim.y blocks of a row, rank 0 the heaviest under the causal mask. The hardware hands
+// consecutive linear workgroup ids to the 8 XCDs in turn. With few blocks per row, every
+// XCD takes its share of all rows, heaviest rank first across rows (the launch order).
+// With many, each XCD takes a contiguous range of rows (items j = row * nb + rank), the
+// heaviest rank first within a row, so that the few rows one XCD works on at a time share
+// its L2: every workgroup of a row streams the same K/V (or Q/dO) blocks, and at long
+// sequences the rows of all heads an XCD would otherwise interleave do not fit in it.
+constexpr int kXcds = 8, kXcdOrderMinBlocks = 32;
+__device__ __forceinline__ void grid_item(int& row, int& rank) {
+  const int R = gridDim.x, nb = gridDim.y;
+  if (nb < kXcdOrderMinBlocks) {
+    row = blockIdx.x;
+    rank = blockIdx.y;
+    return;
+  }
+  const int L = (int)blockIdx.y * R + (int)blockIdx.x, N = R * nb;
+  const int x = L % kXcds, k = L / kXcds, q = N / kXcds, r = N % kXcds;
+  const int j = x * q + min(x, r) + k;   // XCD x owns items [x q + min(x, r), ... + q + (x < r))
+  row = j / nb;
+  rank = j % nb;
+}
 static_assert(kW == 4 || kW == 8, "64-row tiles are staged four rows per load by every wave");
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -180,9 +203,11 @@ void dq_mfma_kernel(AttnParams p) {
   constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
   __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BN * kHD];   // [buffer][K, V]
 
-  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  int row, rank;
+  grid_item(row, rank);
+  const int b = row / p.Hq, h = row % p.Hq;
   const int nqb = (p.Tq + BM - 1) / BM;
-  const int qb = nqb - 1 - (int)blockIdx.y;   // causal: heaviest query block first
+  const int qb = nqb - 1 - rank;   // causal: heaviest query block first
   const int G = p.Hq / p.Hkv, kvh = h / G;
   const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
   const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
@@ -420,9 +445,11 @@ void fwd_mfma_kernel(AttnParams p) {
   constexpr int BN = kRows, QW = 16 * kNT, BM = kW * QW;
   __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BN * kHD];   // [buffer][K, V]
 
-  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  int row, rank;
+  grid_item(row, rank);
+  const int b = row / p.Hq, h = row % p.Hq;
   const int nqb = (p.Tq + BM - 1) / BM;
-  const int qb = nqb - 1 - (int)blockIdx.y;   // causal: heaviest query block first
+  const int qb = nqb - 1 - rank;   // causal: heaviest query block first
   const int G = p.Hq / p.Hkv, kvh = h / G;
   const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
   const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
@@ -631,8 +658,10 @@ void dkdv_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sm[2][2][BM * kHD];   // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float sv[2][2][BM];            // [buffer][lse, D]
 
-  const int b = blockIdx.x / p.Hkv, kvh = blockIdx.x % p.Hkv;
-  const int kb = blockIdx.y * BN;
+  int row, rank;
+  grid_item(row, rank);
+  const int b = row / p.Hkv, kvh = row % p.Hkv;
+  const int kb = rank * BN;   // causal: rank 0 sees every query block
   const int G = p.Hq / p.Hkv;
   const int w = wave_id(), lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
   const int Tq = p.Tq, Tk = p.Tk, off = Tk - Tq;
