@@ -258,6 +258,18 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
     }
   }
 
+  // q and dO of the group's rows (one 8-element piece of each per thread), loaded with the
+  // rest so that every input of the pass is in flight before the first wait
+  constexpr int C8 = D / 8;
+  static_assert(kMaxRows * C8 <= kThreads, "one q and dO piece per thread");
+  const bool has_row = tid < R * C8;
+  frag_t<E> q8, o8;
+  if (has_row) {
+    const int r = tid / C8, c8 = tid % C8;
+    q8 = load8<E>(rp<E>(p.q, p.sq, b, r % Tq, kvh * G + r / Tq) + 8 * c8);
+    o8 = load8<E>(rp<E>(p.dout, p.sdo, b, r % Tq, kvh * G + r / Tq) + 8 * c8);
+  }
+
   // merge every chunk's statistics for each row (16 lanes per row)
   {
     const int r = tid >> 4, cl = tid & 15;
@@ -288,7 +300,14 @@ __global__ __launch_bounds__(kThreads) void decode_grads_kernel(AttnParams p, De
       }
     }
   }
-  stage_rows<E, D>(p, b, kvh, R, &sq[0][0], &sdo[0][0], D);
+  if (has_row) {
+    const int r = tid / C8, c8 = tid % C8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq[r][8 * c8 + e] = to_f32(q8[e]);
+      sdo[r][8 * c8 + e] = to_f32(o8[e]);
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kPairs; ++k) {
