@@ -630,13 +630,15 @@ int layer_bwd(const layer_bwd_cfg* c, const layer_saved* sv, const float* dh_out
   float* ds = reinterpret_cast<float*>(base + 2 * align256(TC));
   float* part = reinterpret_cast<float*>(base + 2 * align256(TC) + align256((size_t)H * T * T * 4));
 
-  // 1. linear backward: dO = dh_out W^T, dW = o^T dh_out
-  int rc = hip_status(vtb::launch_linear_bwd_split(sv->o, sv->w, dh_out, d_o, dw, T, C, C, part, s), "layer linear");
+  // 1. linear backward: dO = dh_out W^T (as split-K partials), dW = o^T dh_out
+  int ns = 1;
+  int rc = hip_status(vtb::launch_linear_bwd_parts(sv->o, sv->w, dh_out, d_o, dw, T, C, C, part, &ns, s), "layer linear");
   if (rc) return rc;
-  // 2. attention backward with the saved softmax: dP = dO V^T, dS = P o (dP - D), then
-  //    dq = scale dS K (workspace), dK = scale dS^T Q, dV = P^T dO
-  rc = hip_status(vtb::launch_attn_saved_p_bwd(sv->q, sv->k, sv->v, d_o, sv->P, ds, dq, dk, dv, T, H, D, C, c->scale,
-                                               c->causal, s),
+  // 2. attention backward with the saved softmax: dO summed from the partials (and kept for
+  //    dV), dP = dO V^T, dS = P o (dP - D), then dq = scale dS K (workspace),
+  //    dK = scale dS^T Q, dV = P^T dO
+  rc = hip_status(vtb::launch_attn_saved_p_bwd_parts(sv->q, sv->k, sv->v, ns > 1 ? part : d_o, ns, (int64_t)T * C, d_o,
+                                                     sv->P, ds, dq, dk, dv, T, H, D, C, C, C, c->scale, c->causal, s),
                   "layer attention");
   if (rc) return rc;
   // 3. dh_in = dh_out + RMSNormBackward(x, gamma, RoPEBackward(dq))
@@ -772,17 +774,18 @@ int attn_block_bwd(const attn_block_cfg* c, const attn_block_saved* sv, const fl
                                          align256(BT * 3 * C * 4));
 
   // 1. output projection: dctx = dx2 Wo^T, gWo = ctx^T dx2
-  int rc = hip_status(vtb::launch_linear_bwd_split(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, s), "block Wo");
+  int ns = 1;
+  int rc = hip_status(vtb::launch_linear_bwd_parts(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, &ns, s), "block Wo");
   if (rc) return rc;
-  // 2. attention backward with the saved softmax, one sequence at a time (dS reused),
-  //    gradients written into the q | k | v thirds of dqkv
+  // 2. attention backward with the saved softmax, one sequence at a time (dS reused), dctx
+  //    summed from the partials on the way, gradients written into the q | k | v thirds of dqkv
   for (int b = 0; b < c->B; ++b) {
     const int64_t r3 = (int64_t)b * Ti * 3 * C, r1 = (int64_t)b * Ti * C;
     const float* q = sv->qkv + r3;
     float* dq = dqkv + r3;
-    rc = hip_status(vtb::launch_attn_saved_p_bwd_ld(q, q + C, q + 2 * C, dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq,
-                                                    dq + C, dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal,
-                                                    s),
+    rc = hip_status(vtb::launch_attn_saved_p_bwd_parts(q, q + C, q + 2 * C, (ns > 1 ? part : dctx) + r1, ns, BT * C,
+                                                       dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq, dq + C,
+                                                       dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal, s),
                     "block attention");
     if (rc) return rc;
   }
@@ -872,16 +875,18 @@ int rms_attn_block_bwd(const rms_attn_block_cfg* c, const rms_attn_block_saved* 
   float* part = carve(0);
 
   // 1. output projection: dctx = dx2 Wo^T, gWo = ctx^T dx2
-  int rc = hip_status(vtb::launch_linear_bwd_split(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, s), "layer Wo");
+  int ns = 1;
+  int rc = hip_status(vtb::launch_linear_bwd_parts(sv->ctx, sv->w_o, dx2, dctx, dw_o, bt, ci, ci, part, &ns, s), "layer Wo");
   if (rc) return rc;
   for (int b = 0; b < c->B; ++b) {
     const int64_t r3 = (int64_t)b * Ti * 3 * C, r1 = (int64_t)b * Ti * C;
     const float* q = sv->qkv + r3;
     float* dq = dqkv + r3;
-    // 2. attention backward with the saved softmax into the q | k | v thirds of dqkv
-    rc = hip_status(vtb::launch_attn_saved_p_bwd_ld(q, q + C, q + 2 * C, dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq,
-                                                    dq + C, dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal,
-                                                    s),
+    // 2. attention backward with the saved softmax into the q | k | v thirds of dqkv, dctx
+    //    summed from the partials on the way
+    rc = hip_status(vtb::launch_attn_saved_p_bwd_parts(q, q + C, q + 2 * C, (ns > 1 ? part : dctx) + r1, ns, BT * C,
+                                                       dctx + r1, sv->P + (int64_t)b * H * T * T, ds, dq, dq + C,
+                                                       dq + 2 * C, Ti, H, D, 3 * ci, ci, 3 * ci, c->scale, c->causal, s),
                     "layer attention");
     if (rc) return rc;
     // 3. RoPE backward on dq and dk in place: their 2H heads are the first 2C columns of

@@ -306,13 +306,14 @@ __global__ __launch_bounds__(256, 4) void gemm_f32_kernel(GemmDesc d0, GemmDesc 
 
 int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG - 1) / BNG) * d.nsplit * d.batch; }
 
-// out[i] = sum over s of part[s * n + i], in order s = 0, 1, ... (four elements per lane)
+// out[i] = sum over s of part[s * stride4 + i], in order s = 0, 1, ... (four elements per
+// lane; stride4 >= n4 in float4 units)
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restrict__ part, int ns, int64_t n4,
-                                                         float4* __restrict__ out) {
+                                                         float4* __restrict__ out, int64_t stride4) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
     float4 a = part[i];
     for (int s = 1; s < ns; ++s) {
-      const float4 b = part[s * n4 + i];
+      const float4 b = part[s * stride4 + i];
       a.x += b.x;
       a.y += b.y;
       a.z += b.z;
@@ -390,7 +391,27 @@ hipError_t launch_linear_bwd_split(const float* x, const float* w, const float* 
   const int64_t n4 = (int64_t)T * K / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(part), ns, n4,
-                     reinterpret_cast<float4*>(dx));
+                     reinterpret_cast<float4*>(dx), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_bwd_parts(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K,
+                                   int N, float* part, int* ns_out, hipStream_t s) {
+  if (T < 1 || K < 1 || N < 1 || !dx || !dw || !ns_out) return hipErrorInvalidValue;
+  const int ns = linear_bwd_splits(T, K, N);
+  if (ns == 1 || ((int64_t)T * K) % 4) {
+    *ns_out = 1;
+    return launch_linear_bwd(x, w, dy, dx, dw, T, K, N, s);
+  }
+  GemmDesc gx, gw;
+  linear_descs(x, w, dy, part, dw, T, K, N, gx, gw);
+  const int nk = (N + KT - 1) / KT;
+  gx.nsplit = ns;
+  gx.kchunk = ((nk + ns - 1) / ns) * KT;
+  gx.c_split = (int64_t)T * K;
+  const int tx = tiles_of(gx), tw = tiles_of(gw);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
+  *ns_out = ns;
   return hipGetLastError();
 }
 
@@ -452,6 +473,141 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows_vec_kernel(const f32x4* 
   }
 }
 
+// dP, D and dS of 16 QB query rows of one head per workgroup, in one kernel:
+//     dO = sum_s part_s (the split-K partials of the product that made it, summed in
+//          chunk order on the way in and written once to dout for the dV product),
+//     dP = dO V^T on the fp32 matrix cores (16x16x4), D = rowsum(P o dP) over the visible
+//     keys, dS = P o (dP - D), zero where invisible,
+// for T <= 256 NT (each wave keeps its tiles' dP in registers). Sixteen waves: wave w takes
+// the 16-key tiles w, w + 16, ... for every 16-row sub-block of the workgroup, so a V tile
+// is loaded once for QB sub-blocks and a workgroup's loads are all in flight at once.
+// Lane (m, g) = (lane % 16, lane / 16) holds d = 16 j + 4 g .. 4 g + 3 of query row m of a
+// sub-block (A, from LDS) and of key row k0 + m (B); step (j, e) contracts
+// d = 16 j + 4 g + e across the four lane groups, so A and B agree on every k. Result
+// register r of a tile is (query 4 g + r of the sub-block, key k0 + m). Causal rows write
+// dS up to the end of their 64-query block (what the following products read), zeros past
+// the visible keys.
+constexpr int kDpWaves = 16, kDpQB = 2;
+template <int DJ, int NT>
+__global__ __launch_bounds__(64 * kDpWaves) void attn_dp_ds_kernel(const float* __restrict__ part, int ns,
+                                                                   int64_t part_stride, float* __restrict__ dout,
+                                                                   const float* __restrict__ v,
+                                                                   const float* __restrict__ P, float* __restrict__ ds,
+                                                                   int T, int ld_do, int ld_in, int causal) {
+  constexpr int D = 16 * DJ, QB = kDpQB, ROWS = 16 * QB;
+  __shared__ float sD[kDpWaves][ROWS];
+  __shared__ __attribute__((aligned(16))) float sA[ROWS][D + 4];   // the block's dO rows
+  const int h = blockIdx.y, q0 = blockIdx.x * ROWS;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, m = lane & 15, g = lane >> 4;
+  const int kvis = causal ? min(T, q0 + ROWS) : T;                  // keys any row of the block sees
+  const int kwrite = causal ? min(T, (q0 / 64 + 1) * 64) : T;       // keys whose dS is written
+  const int ntile = (kwrite + 15) / 16;
+  const float* Ph = P + (int64_t)h * T * T;
+  float* dsh = ds + (int64_t)h * T * T;
+  // every load of the wave first: its V rows and P values (rows and keys past the ends
+  // clamped in bounds; their products are masked)
+  f32x4 bv[NT][DJ], pv[QB][NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int k0 = 16 * (w + kDpWaves * i), key = min(k0 + m, T - 1);
+    const float* vb = v + (int64_t)key * ld_in + h * D + 4 * g;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) bv[i][j] = *reinterpret_cast<const f32x4*>(vb + 16 * j);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[qb][i][r] = Ph[(int64_t)min(q0 + 16 * qb + 4 * g + r, T - 1) * T + key];
+  }
+  // dO rows: the partials summed in chunk order once per workgroup (one float4 per thread
+  // and pass), kept in LDS for every wave's A operand and written to dout for the dV
+  // product; rows past T re-read row T - 1 and are not written.
+  {
+    constexpr int C4 = D / 4;
+    for (int idx = threadIdx.x; idx < ROWS * C4; idx += 64 * kDpWaves) {
+      const int r = idx / C4, c4 = idx % C4;
+      const float* src = part + (int64_t)min(q0 + r, T - 1) * ld_do + h * D + 4 * c4;
+      f32x4 x = *reinterpret_cast<const f32x4*>(src);
+      for (int sp = 1; sp < ns; ++sp) x += *reinterpret_cast<const f32x4*>(src + sp * part_stride);
+      *reinterpret_cast<f32x4*>(&sA[r][4 * c4]) = x;
+      if (q0 + r < T && dout != part) *reinterpret_cast<f32x4*>(dout + (int64_t)(q0 + r) * ld_do + h * D + 4 * c4) = x;
+    }
+  }
+  __syncthreads();
+  f32x4 dp[QB][NT];
+  float dsum[QB][4] = {};
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int k0 = 16 * (w + kDpWaves * i), key = k0 + m;
+      dp[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k0 < min(kvis, q0 + 16 * qb + 16) || !causal) {   // uniform over the wave
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+          const f32x4 aj = *reinterpret_cast<const f32x4*>(&sA[16 * qb + m][16 * j + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[qb][i] = __builtin_amdgcn_mfma_f32_16x16x4f32(aj[e], bv[i][j][e], dp[qb][i], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = q0 + 16 * qb + 4 * g + r;
+        const bool vis = q < T && key < T && (!causal || key <= q);
+        pv[qb][i][r] = vis ? pv[qb][i][r] : 0.f;
+        dsum[qb][r] = fmaf(pv[qb][i][r], dp[qb][i][r], dsum[qb][r]);
+      }
+    }
+  }
+  // D per query: the 16 lanes of a group hold other keys of the same rows, then the waves
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) dsum[qb][r] += __shfl_xor(dsum[qb][r], o, 64);
+    }
+  if (m == 0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sD[w][16 * qb + 4 * g + r] = dsum[qb][r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float Dq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kDpWaves; ++ww) t += sD[ww][16 * qb + 4 * g + r];
+      Dq[r] = t;
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = w + kDpWaves * i, key = 16 * t + m;
+      if (t < ntile && key < T) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = q0 + 16 * qb + 4 * g + r;
+          if (q < T) dsh[(int64_t)q * T + key] = pv[qb][i][r] * (dp[qb][i][r] - Dq[r]);   // pv = 0 where invisible
+        }
+      }
+    }
+  }
+}
+
+template <int DJ>
+void launch_dp_ds(int nt, dim3 grid, hipStream_t s, const float* part, int ns, int64_t ps, float* dout, const float* v,
+                  const float* P, float* ds, int T, int ld_do, int ld_in, int causal) {
+  if (nt <= 1)
+    hipLaunchKernelGGL((attn_dp_ds_kernel<DJ, 1>), grid, dim3(64 * kDpWaves), 0, s, part, ns, ps, dout, v, P, ds, T, ld_do,
+                       ld_in, causal);
+  else
+    hipLaunchKernelGGL((attn_dp_ds_kernel<DJ, 2>), grid, dim3(64 * kDpWaves), 0, s, part, ns, ps, dout, v, P, ds, T, ld_do,
+                       ld_in, causal);
+}
+
 }  // namespace
 
 hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* v, const float* dout, const float* P,
@@ -460,11 +616,13 @@ hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* 
   return launch_attn_saved_p_bwd_ld(q, k, v, dout, P, ds, dq, dk, dv, T, H, D, ld, ld, ld, scale, causal, s);
 }
 
-hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const float* v, const float* dout, const float* P,
-                                      float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld_in,
-                                      int ld_do, int ld_out, float scale, int causal, hipStream_t s) {
-  if (T < 1 || H < 1 || D < 1 || ld_in < H * D || ld_do < H * D || ld_out < H * D) return hipErrorInvalidValue;
-  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld_in % 4 == 0 && ld_do % 4 == 0 && ld_out % 4 == 0;
+namespace {
+
+// dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO per head, contraction limited to the
+// visible keys (dQ) or queries (dK, dV); one launch.
+hipError_t launch_attn_dqkv(const float* q, const float* k, const float* dout, const float* P, const float* ds, float* dq,
+                            float* dk, float* dv, int T, int H, int D, int ld_in, int ld_do, int ld_out, float scale,
+                            int causal, bool v4, hipStream_t s) {
   auto base = [&](GemmDesc& g) {
     g = GemmDesc{};
     g.nsplit = 1;
@@ -473,9 +631,41 @@ hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const floa
     g.alpha = 1.f;
     g.vec = v4;
   };
-  // dP = dO V^T per head, on the (query, key) tiles that hold a visible pair
-  GemmDesc gp;
-  base(gp);
+  GemmDesc gq, gk;
+  base(gq);
+  gq.A = ds; gq.am = T; gq.ak = 1; gq.a_kc = 1; gq.a_b = (int64_t)T * T;
+  gq.B = k; gq.bk = ld_in; gq.bn = 1; gq.b_kc = 0; gq.b_b = D;
+  gq.C = dq; gq.ldc = ld_out; gq.c_b = D;
+  gq.M = T; gq.N = D; gq.K = T; gq.kchunk = T;
+  gq.alpha = scale;
+  gq.tri = causal ? TRI_KLE : TRI_NONE;
+  base(gk);
+  gk.A = ds; gk.am = 1; gk.ak = T; gk.a_kc = 0; gk.a_b = (int64_t)T * T;
+  gk.B = q; gk.bk = ld_in; gk.bn = 1; gk.b_kc = 0; gk.b_b = D;
+  gk.C = dk; gk.ldc = ld_out; gk.c_b = D;
+  gk.M = T; gk.N = D; gk.K = T; gk.kchunk = T;
+  gk.alpha = scale;
+  gk.tri = causal ? TRI_KGE : TRI_NONE;
+  GemmDesc gv = gk;
+  gv.A = P;
+  gv.B = dout;
+  gv.bk = ld_do;
+  gv.C = dv;
+  gv.alpha = 1.f;
+  const int t0 = tiles_of(gq), t1 = tiles_of(gk), t2 = tiles_of(gv);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(t0 + t1 + t2), dim3(256), 0, s, gq, gk, gv, t0, t1);
+  return hipGetLastError();
+}
+
+// dP = dO V^T per head on the (query, key) tiles that hold a visible pair, then the dS rows.
+void launch_dp_then_ds_rows(const float* v, const float* dout, const float* P, float* ds, int T, int H, int D, int ld_in,
+                            int ld_do, int causal, bool v4, hipStream_t s) {
+  GemmDesc gp = GemmDesc{};
+  gp.nsplit = 1;
+  gp.c_split = 0;
+  gp.batch = H;
+  gp.alpha = 1.f;
+  gp.vec = v4;
   gp.A = dout; gp.am = ld_do; gp.ak = 1; gp.a_kc = 1; gp.a_b = D;
   gp.B = v; gp.bk = 1; gp.bn = ld_in; gp.b_kc = 1; gp.b_b = D;
   gp.C = ds; gp.ldc = T; gp.c_b = (int64_t)T * T;
@@ -494,32 +684,52 @@ hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const floa
                        reinterpret_cast<const f32x4*>(P), reinterpret_cast<f32x4*>(ds), rows, T, causal);
   else
     hipLaunchKernelGGL(softmax_bwd_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, P, ds, rows, T, causal);
-  // dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO per head, contraction limited to the
-  // visible keys (dQ) or queries (dK, dV)
-  GemmDesc gq, gk, gv;
-  base(gq);
-  gq.A = ds; gq.am = T; gq.ak = 1; gq.a_kc = 1; gq.a_b = (int64_t)T * T;
-  gq.B = k; gq.bk = ld_in; gq.bn = 1; gq.b_kc = 0; gq.b_b = D;
-  gq.C = dq; gq.ldc = ld_out; gq.c_b = D;
-  gq.M = T; gq.N = D; gq.K = T; gq.kchunk = T;
-  gq.alpha = scale;
-  gq.tri = causal ? TRI_KLE : TRI_NONE;
-  base(gk);
-  gk.A = ds; gk.am = 1; gk.ak = T; gk.a_kc = 0; gk.a_b = (int64_t)T * T;
-  gk.B = q; gk.bk = ld_in; gk.bn = 1; gk.b_kc = 0; gk.b_b = D;
-  gk.C = dk; gk.ldc = ld_out; gk.c_b = D;
-  gk.M = T; gk.N = D; gk.K = T; gk.kchunk = T;
-  gk.alpha = scale;
-  gk.tri = causal ? TRI_KGE : TRI_NONE;
-  gv = gk;
-  gv.A = P;
-  gv.B = dout;
-  gv.bk = ld_do;
-  gv.C = dv;
-  gv.alpha = 1.f;
-  const int t0 = tiles_of(gq), t1 = tiles_of(gk), t2 = tiles_of(gv);
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3(t0 + t1 + t2), dim3(256), 0, s, gq, gk, gv, t0, t1);
-  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const float* v, const float* dout, const float* P,
+                                      float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld_in,
+                                      int ld_do, int ld_out, float scale, int causal, hipStream_t s) {
+  if (T < 1 || H < 1 || D < 1 || ld_in < H * D || ld_do < H * D || ld_out < H * D) return hipErrorInvalidValue;
+  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld_in % 4 == 0 && ld_do % 4 == 0 && ld_out % 4 == 0;
+  launch_dp_then_ds_rows(v, dout, P, ds, T, H, D, ld_in, ld_do, causal, v4, s);
+  return launch_attn_dqkv(q, k, dout, P, ds, dq, dk, dv, T, H, D, ld_in, ld_do, ld_out, scale, causal, v4, s);
+}
+
+bool attn_dp_ds_fused_applicable(int T, int D, int ld_in, int ld_do, const void* part, const void* v) {
+  return T >= 1 && T <= 2 * 16 * kDpWaves && (D == 32 || D == 64 || D == 128) && ld_in % 4 == 0 && ld_do % 4 == 0 &&
+         ((uintptr_t)part | (uintptr_t)v) % 16 == 0;
+}
+
+hipError_t launch_attn_saved_p_bwd_parts(const float* q, const float* k, const float* v, const float* part, int ns,
+                                         int64_t part_stride, float* dout, const float* P, float* ds, float* dq,
+                                         float* dk, float* dv, int T, int H, int D, int ld_in, int ld_do, int ld_out,
+                                         float scale, int causal, hipStream_t s) {
+  if (T < 1 || H < 1 || D < 1 || ns < 1 || ld_in < H * D || ld_do < H * D || ld_out < H * D) return hipErrorInvalidValue;
+  const bool v4 = T % 4 == 0 && D % 4 == 0 && ld_in % 4 == 0 && ld_do % 4 == 0 && ld_out % 4 == 0;
+  if (attn_dp_ds_fused_applicable(T, D, ld_in, ld_do, part, v) && (ns == 1 || part_stride % 4 == 0) &&
+      (uintptr_t)dout % 16 == 0) {
+    const dim3 grid((T + 16 * kDpQB - 1) / (16 * kDpQB), H);
+    const int nt = (T + 16 * kDpWaves - 1) / (16 * kDpWaves);   // 16-key tiles per wave
+    if (D == 32) launch_dp_ds<2>(nt, grid, s, part, ns, part_stride, dout, v, P, ds, T, ld_do, ld_in, causal);
+    else if (D == 64) launch_dp_ds<4>(nt, grid, s, part, ns, part_stride, dout, v, P, ds, T, ld_do, ld_in, causal);
+    else launch_dp_ds<8>(nt, grid, s, part, ns, part_stride, dout, v, P, ds, T, ld_do, ld_in, causal);
+  } else {
+    if (ns > 1 || dout != part) {   // dO = sum of the partials, then the two-launch dP / dS form
+      if (ld_do != H * D || ((int64_t)T * ld_do) % 4 || part_stride % 4 || part_stride < (int64_t)T * ld_do ||
+          ((uintptr_t)part | (uintptr_t)dout) % 16)
+        return hipErrorInvalidValue;
+      const int64_t n4 = (int64_t)T * ld_do / 4;
+      const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
+      hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(part), ns, n4,
+                         reinterpret_cast<float4*>(dout), part_stride / 4);
+    }
+    launch_dp_then_ds_rows(v, dout, P, ds, T, H, D, ld_in, ld_do, causal, v4, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_dqkv(q, k, dout, P, ds, dq, dk, dv, T, H, D, ld_in, ld_do, ld_out, scale, causal, v4, s);
 }
 
 }  // namespace vtb

@@ -147,5 +147,18 @@ hipError_t launch_attn_saved_p_bwd(const float* q, const float* k, const float* 
 hipError_t launch_attn_saved_p_bwd_ld(const float* q, const float* k, const float* v, const float* dout, const float* P,
                                       float* ds, float* dq, float* dk, float* dv, int T, int H, int D, int ld_in,
                                       int ld_do, int ld_out, float scale, int causal, hipStream_t s);
+// The linear backward with dX's split-K partials left in part (ns_out = their count; 1
+// means dX went straight to dx and part is unused), for a consumer that sums them itself.
+hipError_t launch_linear_bwd_parts(const float* x, const float* w, const float* dy, float* dx, float* dw, int T, int K,
+                                   int N, float* part, int* ns_out, hipStream_t s);
+// Attention backward with a saved P whose dO arrives as ns split-K partials (part + s
+// part_stride, rows of ld_do; ns = 1: part is dO itself). For T <= 512 and D in {32, 64,
+// 128} one kernel sums the partials, writes dO to dout (for dV), forms dP on the matrix
+// cores and D and dS in its epilogue; otherwise the partials are summed into dout and the
+// dP product and the dS rows run as two launches. Then the dQ/dK/dV launch.
+hipError_t launch_attn_saved_p_bwd_parts(const float* q, const float* k, const float* v, const float* part, int ns,
+                                         int64_t part_stride, float* dout, const float* P, float* ds, float* dq,
+                                         float* dk, float* dv, int T, int H, int D, int ld_in, int ld_do, int ld_out,
+                                         float scale, int causal, hipStream_t s);
 
 }  // namespace vtb
