@@ -24,7 +24,7 @@ def _case(B, T, H, d, causal, seed):
 
 # B, T, H, d, causal: one tile, ragged token counts and widths, two sequences, no mask
 BLOCK_CASES = [(2, 1, 2, 8, True), (1, 16, 2, 8, True), (2, 37, 3, 12, True), (2, 64, 4, 32, False), (1, 100, 2, 64, True),
-               (3, 5, 1, 4, True), (1, 300, 2, 16, True)]
+               (3, 5, 1, 4, True), (1, 300, 2, 16, True), (1, 500, 1, 128, True), (2, 48, 12, 128, False)]
 
 
 @pytest.mark.parametrize("B,T,H,d,causal", BLOCK_CASES)

@@ -30,7 +30,11 @@ def _case(B, T, H, d, causal, layout, seed, w_std=None):
 # B, T, H, d, causal, RoPE layout: one token, ragged token counts and widths, several
 # sequences, no mask, split-half pairs
 CASES = [(2, 1, 2, 8, True, 0), (1, 16, 2, 8, True, 0), (2, 37, 3, 12, True, 1), (2, 64, 4, 32, False, 0),
-         (1, 100, 2, 64, True, 1), (3, 5, 1, 4, True, 0), (1, 300, 2, 16, True, 0)]
+         (1, 100, 2, 64, True, 1), (3, 5, 1, 4, True, 0), (1, 300, 2, 16, True, 0),
+         # the one-kernel dO/dP/dS step with two key tiles per wave (256 < T <= 512), causal and not
+         (1, 300, 2, 32, True, 0), (1, 264, 1, 64, False, 1),
+         # C = 1536: the output projection's dX comes in two split-K partials, summed per sequence
+         (2, 64, 12, 128, True, 0)]
 
 
 @pytest.mark.parametrize("B,T,H,d,causal,layout", CASES)
