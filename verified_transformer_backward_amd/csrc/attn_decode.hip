@@ -189,23 +189,33 @@ __global__ __launch_bounds__(kThreads) void decode_chunk_kernel(AttnParams p, De
   }
   __syncthreads();
 
-  // A_c, B_c: thread = four columns, rows r = rg2, rg2 + RG, ...
-  constexpr int C4 = D / 4, RG = kThreads / C4;
-  const int c4 = tid % C4, rg2 = tid / C4;
+  // A_c, B_c: wave w takes rows w, w + 4, ...; lane = (key part ks, four columns c4), the
+  // KS parts of the chunk's keys summed over lanes in a fixed order (part 0 + part 1, then
+  // + the sum of parts 2 and 3), so every wave works when R < 8.
+  constexpr int C4 = D / 4, KS = 64 / C4, KL = kCH / KS;
+  static_assert(C4 * KS == 64 && KS * KL == kCH, "one wave covers the row");
+  const int c4 = lane % C4, ks = lane / C4;
   const int64_t rows = (int64_t)p.B * p.Hq * Tq;
-  for (int r = rg2; r < R; r += RG) {
+  for (int r = w; r < R; r += kThreads / 64) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a;
 #pragma unroll 8
-    for (int k = 0; k < kCH; ++k) {
+    for (int k = ks * KL; k < ks * KL + KL; ++k) {
       const float4 kv = *reinterpret_cast<const float4*>(skv + k * LD + 4 * c4);
       const float x = sx[r * kCH + k], w = sw[r * kCH + k];
       a.x = fmaf(x, kv.x, a.x); a.y = fmaf(x, kv.y, a.y); a.z = fmaf(x, kv.z, a.z); a.w = fmaf(x, kv.w, a.w);
       bb.x = fmaf(w, kv.x, bb.x); bb.y = fmaf(w, kv.y, bb.y); bb.z = fmaf(w, kv.z, bb.z); bb.w = fmaf(w, kv.w, bb.w);
     }
-    const int h = kvh * G + r / Tq, i = r % Tq;
-    const int64_t o = ((int64_t)ch * rows + ((int64_t)b * p.Hq + h) * Tq + i) * D + 4 * c4;
-    *reinterpret_cast<float4*>(ws.a + o) = a;
-    *reinterpret_cast<float4*>(ws.bk + o) = bb;
+#pragma unroll
+    for (int o = C4; o < 64; o <<= 1) {
+      a.x += __shfl_xor(a.x, o, 64); a.y += __shfl_xor(a.y, o, 64); a.z += __shfl_xor(a.z, o, 64); a.w += __shfl_xor(a.w, o, 64);
+      bb.x += __shfl_xor(bb.x, o, 64); bb.y += __shfl_xor(bb.y, o, 64); bb.z += __shfl_xor(bb.z, o, 64); bb.w += __shfl_xor(bb.w, o, 64);
+    }
+    if (ks == 0) {
+      const int h = kvh * G + r / Tq, i = r % Tq;
+      const int64_t o = ((int64_t)ch * rows + ((int64_t)b * p.Hq + h) * Tq + i) * D + 4 * c4;
+      *reinterpret_cast<float4*>(ws.a + o) = a;
+      *reinterpret_cast<float4*>(ws.bk + o) = bb;
+    }
   }
 }
 
