@@ -161,9 +161,11 @@ def _layer_case(layer, T, H, d):
     return saved32, sc
 
 
-# one token (every product has a single row or a one-deep contraction), a ragged shape and a
-# two-tile one
-@pytest.mark.parametrize("T,H,d", [(1, 2, 64), (64, 2, 64), (100, 3, 128)])
+# one token (every product has a single row or a one-deep contraction), a ragged shape, a
+# two-tile one; T 512 (the one-kernel dO/dP/dS step at its largest, two full 16-key tiles
+# per wave) and T 520 (past it: the split-K sum, dP product and dS rows as three
+# launches)
+@pytest.mark.parametrize("T,H,d", [(1, 2, 64), (64, 2, 64), (100, 3, 128), (512, 2, 64), (520, 1, 64)])
 def test_layer_bwd_small(T, H, d):
     need_gpu()
     say(f"layer_bwd T {T} H {H} d {d}")
