@@ -235,3 +235,17 @@ def test_bf16_elementwise_entry_points_validate():
     assert L.rope_bwd_ex(1, A0, A1, 0, 2, 8, 16, None, 0, 10000.0, 0, None) == 0        # no tokens
     assert L.rmsnorm_bwd_ex(1, A0, A1, A2, A0, 4, 64, 1e-6, None) == 3                  # dx aliases x
     assert L.rmsnorm_bwd_ex(9, A0, A1, A2, A3, 4, 64, 1e-6, None) == 1
+
+
+def test_attn_bwd_timed_validation_codes():
+    # the events are checked first (four handles needed), then the same validation as attn_bwd
+    L = vtb.lib()
+    d = _desc()
+    args = (ctypes.byref(d), A0, A1, A2, A3, None, None, A4, A5, A6, WS, 1 << 30, None)
+    ev = (ctypes.c_void_p * 4)(A0, A1, A2, A3)
+    assert L.attn_bwd_timed(*args, None, 4) == 1
+    assert L.attn_bwd_timed(*args, ev, 3) == 1
+    assert b"4 events" in L.vtb_last_error()
+    bad = _desc(D=96)
+    assert L.attn_bwd_timed(ctypes.byref(bad), A0, A1, A2, A3, None, None, A4, A5, A6, WS, 1 << 30, None, ev, 4) == 2
+    assert L.attn_bwd_timed(ctypes.byref(d), A0, A1, A2, A3, None, None, A0, A5, A6, WS, 1 << 30, None, ev, 4) == 3
