@@ -207,3 +207,19 @@ def test_rmsnorm_rows_match_autograd():
     y = torch.tensor(gamma) * xt / torch.sqrt((xt * xt).mean(-1, keepdim=True) + eps)
     (y * torch.tensor(dy)).sum().backward()
     np.testing.assert_allclose(rmsnorm_backward_rows(x, gamma, dy, eps), xt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_scaled_dot_vjps_match_central_differences_and_fail_when_transposed():
+    # scaledDotForward / scaledDotBackwardQ / scaledDotBackwardK ("Hesper.Training.VerifiedBackward",
+    # section "Scaled Dot-Product"): the loss dscore * score differentiated by differences,
+    # and the q and k gradients swapped (a plausible mistake) must not pass
+    from oracle import verify
+    rng = np.random.default_rng(31)
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    sc, dscore = 0.25, -1.7
+    num_q = verify.numerical_grad(lambda z: dscore * specs.scaled_dot_forward(z, k, sc), q, eps=1e-6)
+    num_k = verify.numerical_grad(lambda z: dscore * specs.scaled_dot_forward(q, z, sc), k, eps=1e-6)
+    np.testing.assert_allclose(specs.scaled_dot_backward_q(k, sc, dscore), num_q, rtol=1e-8, atol=1e-9)
+    np.testing.assert_allclose(specs.scaled_dot_backward_k(q, sc, dscore), num_k, rtol=1e-8, atol=1e-9)
+    assert np.max(np.abs(specs.scaled_dot_backward_q(q, sc, dscore) - num_q)) > 1e-2
+    assert specs.scaled_dot_forward(q, k, sc) == pytest.approx(sc * float(np.sum(q * k)), rel=1e-14)
