@@ -304,3 +304,29 @@ def test_optional_dk_dv(case):
             assert torch.equal(dk, full[1])
         if want_dv:
             assert torch.equal(dv, full[2])
+
+
+@pytest.mark.parametrize("workload,reps", [("causal_train", 5), ("decode_gqa", 5), ("long_causal", 2)])
+def test_full_size_repeats_bitwise(workload, reps):
+    """The full-size workloads give one result bit for bit, call after call, with other GPU
+    work between the calls: every sum runs in a fixed order and nothing uses atomics."""
+    need_gpu()
+    say(f"{workload}: {reps} calls, each compared bit for bit with the first")
+    if workload == "causal_train":
+        x, dtype, causal = synth.causal_inputs(), "bf16", True
+    elif workload == "decode_gqa":
+        x, dtype, causal = synth.decode_gqa_inputs(), "f32", False
+    else:
+        x, dtype, causal = synth.long_causal_inputs(), "bf16", True
+    t = {n: dev(x[n], dtype) for n in ("q", "k", "v", "dout")}
+    sc = float(x["scale"])
+    lse = vtb.attn_fwd_lse(t["q"], t["k"], sc, causal) if dtype == "bf16" else None
+    first = vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, causal, lse=lse)
+    torch.cuda.synchronize()
+    for r in range(1, reps):
+        torch.randn(1 << 22, device="cuda").sum()           # unrelated work on the device between calls
+        got = vtb.attn_bwd(t["q"], t["k"], t["v"], t["dout"], sc, causal, lse=lse)
+        torch.cuda.synchronize()
+        for n, a, b in zip(("dq", "dk", "dv"), got, first):
+            assert torch.equal(a, b), f"{workload} call {r}: {n} differs from the first call"
+    say(f"{workload}: {reps} calls identical")
