@@ -58,7 +58,8 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 bool valid_dtype(int32_t d) { return d == VTB_F32 || d == VTB_BF16; }
 size_t esize(int32_t d) { return d == VTB_BF16 ? 2 : 4; }
 
-// Workspace carve-up of the flash path: row term D, computed lse.
+// Workspace carve-up of the flash path: row term D, computed lse (or, on the MFMA path
+// where lse is given, lse in base-2 units for the dk/dv pass).
 struct FlashWs {
   size_t dlt, lse, total;
 };
@@ -264,10 +265,12 @@ int attn_bwd_impl(const attn_bwd_desc* d, const void* q, const void* k, const vo
     mode = vtb::ROW_LSE_COMPUTE;
   }
   const bool mfma = vtb::mfma_path_applicable(p);
-  if (mfma && (mode == vtb::ROW_LSE_GIVEN || mode == vtb::ROW_D_GIVEN))
+  if (mfma && (mode == vtb::ROW_LSE_GIVEN || mode == vtb::ROW_D_GIVEN)) {
+    p.lse2 = reinterpret_cast<float*>(base + w.lse);   // free when lse is given
     rc = hip_status(vtb::launch_mfma_dq(p, s, ev.pass(0), mode == vtb::ROW_D_GIVEN), "dq pass");
-  else
+  } else {
     rc = hip_status(vtb::launch_flash_dq(p, mode, s, ev.pass(0)), "flash dq pass");
+  }
   if (rc) return rc;
   if (!dk && !dv) return VTB_OK;   // only dQ wanted: the key-parallel pass is skipped
   if (mfma && !P) return hip_status(vtb::launch_mfma_dkdv(p, s, ev.pass(1)), "dk/dv pass");

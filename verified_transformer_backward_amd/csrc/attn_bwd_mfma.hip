@@ -16,6 +16,8 @@
 //         delta_ij (k_j - B_i) rather than delta_ij k_j, and a row whose dS vanishes
 //         (a single visible key) gets dQ = 0 exactly. The D written for the dk/dv pass
 //         is the fp32 sum, exact enough that dS = P o (dP - D) vanishes there too.
+//         Also writes lse * log2(e) per row, so that the dk/dv pass forms P = exp2(...)
+//         without a multiply per element.
 //   dkdv  key-parallel over query blocks (of every q-head of the kv-head's group):
 //         S, dP, then dV += P^T dO and dK += dS^T Q with dS = P o (dP - D), D from dq.
 //
@@ -351,12 +353,26 @@ void dq_mfma_kernel(AttnParams p) {
         for (int r = 0; r < 4; ++r) {
           const float pr = pe[kt][qt][r];
           const float x = DG ? pr * (dT[kt][qt][r] - dg[qt]) : pr * dT[kt][qt][r];
-          const __bf16 xr = (__bf16)x;
           dsum[qt] += x;
-          dsum_r[qt] += (float)xr;
           pb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)pr;
-          xb[kt >> 1][qt][4 * (kt & 1) + r] = xr;
+          xb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)x;
         }
+    // The rounded sum, two terms per instruction: each bf16 pair dotted with (1, 1).
+    if constexpr (!DG) {
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int qt = 0; qt < kNT; ++qt) {
+          const bf16x8 x8 = xb[c][qt];
+          float t = dsum_r[qt];
+          t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x8, x8, 0, 1), one2, t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x8, x8, 2, 3), one2, t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x8, x8, 4, 5), one2, t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x8, x8, 6, 7), one2, t, false);
+          dsum_r[qt] = t;
+        }
+    }
     fence();
     prio_mfma();
     // A^T += K^T (P o dP)^T,  B^T += K^T P^T over (dt, c) pairs, reads AHEAD pairs ahead
@@ -414,7 +430,10 @@ void dq_mfma_kernel(AttnParams p) {
     dr += __shfl_xor(dr, 32, 64);
     Dq[qt] = DG ? 0.f : dr;   // with D from O, A already holds (P o (dP - D)) K
     const int i = qw0 + 16 * qt + lc;
-    if (lg == 0 && i < Tq) p.dlt[rowbase + i] = DG ? dg[qt] : d;
+    if (lg == 0 && i < Tq) {
+      p.dlt[rowbase + i] = DG ? dg[qt] : d;
+      p.lse2[rowbase + i] = lse2[qt];   // the dk/dv pass reads lse in base-2 units
+    }
   }
   // dQ = scale (A - D B): the lane holds d = 16 dt + 4 lg + r of query qw0 + 16 qt + lc.
 #pragma unroll
@@ -652,6 +671,9 @@ void fwd_mfma_kernel(AttnParams p) {
 // block) that sees the keys: S = Q K^T, dP = dO V^T (queries as MFMA rows), P and dS
 // with the block's lse and D, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
 // from LDS transpose reads. dK and dV are written once, in a fixed head order.
+// L2: lse is read from p.lse2 (already times log2 e, written by the dq pass); otherwise
+// from p.lse.
+template <bool L2>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void dkdv_mfma_kernel(AttnParams p) {
   constexpr int BM = kRows, KW = 16 * kNT, BN = kW * KW;
@@ -707,7 +729,7 @@ void dkdv_mfma_kernel(AttnParams p) {
     qst.stage(sm_lds + (2 * buf) * kTileBytes, Qh, p.sq[1], q0, Tq);
     ost.stage(sm_lds + (2 * buf + 1) * kTileBytes, Oh, p.sdo[1], q0, Tq);
     const int64_t rb = ((int64_t)b * p.Hq + hh) * Tq;
-    if (w == 0) stage_vals64(sv_lds + (2 * buf) * kValBytes, p.lse + rb, q0, Tq);
+    if (w == 0) stage_vals64(sv_lds + (2 * buf) * kValBytes, (L2 ? p.lse2 : p.lse) + rb, q0, Tq);
     if (w == 1) stage_vals64(sv_lds + (2 * buf + 1) * kValBytes, p.dlt + rb, q0, Tq);
   };
 
@@ -775,7 +797,7 @@ void dkdv_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pe[qt][kt][r] = __builtin_amdgcn_exp2f(S[qt][kt][r] * sl2 - Lv[qt][r] * kLog2e);
+        for (int r = 0; r < 4; ++r) pe[qt][kt][r] = __builtin_amdgcn_exp2f(S[qt][kt][r] * sl2 - (L2 ? Lv[qt][r] : Lv[qt][r] * kLog2e));
     if (!full) {
       asm volatile("");   // keeps the masking inside the branch (no speculation into full blocks)
 #pragma unroll
@@ -847,7 +869,7 @@ void dkdv_mfma_kernel(AttnParams p) {
     auto dma = [&](int part) {
       if (!more || part != 0) return;
       const int64_t rb = ((int64_t)b * p.Hq + hs) * Tq;
-      if (w == 0) stage_vals64(sv_lds + (2 * nxt) * kValBytes, p.lse + rb, qn, Tq);
+      if (w == 0) stage_vals64(sv_lds + (2 * nxt) * kValBytes, (L2 ? p.lse2 : p.lse) + rb, qn, Tq);
       if (w == 1) stage_vals64(sv_lds + (2 * nxt + 1) * kValBytes, p.dlt + rb, qn, Tq);
       qst.stage(sm_lds + (2 * nxt) * kTileBytes, Qn, p.sq[1], qn, Tq);
       ost.stage(sm_lds + (2 * nxt + 1) * kTileBytes, On, p.sdo[1], qn, Tq);
@@ -926,7 +948,10 @@ hipError_t launch_mfma_dq(const AttnParams& p, hipStream_t s, KernelEvents ev, b
 hipError_t launch_mfma_dkdv(const AttnParams& p, hipStream_t s, KernelEvents ev) {
   constexpr int BN = kW * 16 * kNT;
   const dim3 grid(p.B * p.Hkv, (p.Tk + BN - 1) / BN);
-  launch_kernel(dkdv_mfma_kernel, grid, dim3(kT), 0, s, ev, p);
+  if (p.lse2)
+    launch_kernel(dkdv_mfma_kernel<true>, grid, dim3(kT), 0, s, ev, p);
+  else
+    launch_kernel(dkdv_mfma_kernel<false>, grid, dim3(kT), 0, s, ev, p);
   return hipGetLastError();
 }
 

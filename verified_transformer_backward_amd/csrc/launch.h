@@ -20,6 +20,7 @@ struct AttnParams {
   const void* o;      // the forward's saved output [B, Tq, Hq, D] (ROW_D_GIVEN), strides so
   float* lse_out;     // where a pass that computes lse writes it
   float* dlt;         // workspace [B, Hq, Tq]: D_i = rowsum(P o dP)
+  float* lse2;        // workspace [B, Hq, Tq]: lse_i * log2(e), written by the MFMA dq pass for its dk/dv pass
   void* dq;
   void* dk;
   void* dv;
