@@ -129,6 +129,33 @@ def test_linear_shapes(T, K, N):
     assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
 
 
+@pytest.mark.parametrize("want_dx,want_dw", [(True, True), (False, True)])
+def test_linear_large_tiles(want_dx, want_dw):
+    """T 2048, K = N = 4096: 1536 (both products) or 1024 (dW alone) tiles of 128 x 128, so the
+    launch takes the large-tile kernel (k-contiguous dX operands, r-contiguous dW operands
+    transposed in registers). Sampled rows of dX and dW, across tile edges, against the
+    oracle; a second call bitwise equal."""
+    need_gpu()
+    T, K, N = 2048, 4096, 4096
+    say(f"linear large tiles T {T} K {K} N {N} dx {want_dx} dw {want_dw}")
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    dy = rng.standard_normal((T, N)).astype(np.float32)
+    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    dx, dw = vtb.linear_bwd(xd, wd, dyd, want_dx=want_dx, want_dw=want_dw)
+    torch.cuda.synchronize()
+    x64, w64, dy64 = (a.astype(np.float64) for a in (x, w, dy))
+    if want_dx:
+        rows = np.array([0, 1, 63, 64, 127, 128, 1000, 1919, 2047])
+        assert_close("linear.dx rows", host(dx)[rows], dy64[rows] @ w64.T, TOL["f32"])
+    rows = np.array([0, 5, 127, 128, 255, 2049, 3071, 4095])
+    assert_close("linear.dw rows", host(dw)[rows], x64[:, rows].T @ dy64, TOL["f32"])
+    dx2, dw2 = vtb.linear_bwd(xd, wd, dyd, want_dx=want_dx, want_dw=want_dw)
+    torch.cuda.synchronize()
+    assert torch.equal(dw, dw2) and (not want_dx or torch.equal(dx, dx2))
+
+
 def test_linear_repeats_bitwise():
     """30 calls at the layer-chain shape give one bitwise result: a barrier that does not
     wait for another wave's LDS stores shows up here as a few wrong 32 x 16 tiles."""

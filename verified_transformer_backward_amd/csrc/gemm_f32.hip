@@ -8,7 +8,8 @@
 // One launch holds the tiles of both products: dX tiles first (their contraction is the
 // long one), then dW tiles. Each 256-thread workgroup computes a 64 x 64 tile; each wave
 // a 32 x 32 quarter as 2 x 2 MFMA tiles. A and B tiles are staged in LDS k-contiguous,
-// transposing on the way in when the global operand is m- or n-contiguous.
+// transposing on the way in when the global operand is m- or n-contiguous. Large linear
+// products whose tiles all lie inside the matrices take 128 x 128 tiles instead (below).
 #include "device_common.h"
 #include "launch.h"
 
@@ -306,6 +307,190 @@ __global__ __launch_bounds__(256, 4) void gemm_f32_kernel(GemmDesc d0, GemmDesc 
 
 int tiles_of(const GemmDesc& d) { return ((d.M + BMG - 1) / BMG) * ((d.N + BNG - 1) / BNG) * d.nsplit * d.batch; }
 
+// ------------------------------------------------------------------ 128 x 128 tiles
+// Products whose tiles all lie inside the matrices (M and N multiples of 128, every
+// contraction chunk a multiple of KT, float4 rows) and that give enough tiles to keep both
+// workgroup slots of every CU busy take 128 x 128 tiles. Each wave computes a 64 x 64
+// quarter as 4 x 4 MFMA tiles: every operand fragment read from LDS feeds four MFMA tiles
+// instead of two, and a k step carries four times the MFMAs of a 64 x 64 tile per barrier
+// and per global load. One register set holds the next k step (a step's 128 MFMAs per wave
+// outlast its loads). An r-contiguous operand is loaded as 4 x 4 blocks (four float4 along
+// r at four consecutive k) and stored k-contiguous, one float4 per row (a transpose in
+// registers), so every LDS store is 16 bytes wide.
+constexpr int BMB = 128;
+constexpr int kBigMinTiles = 1024;   // 2 workgroups per CU, each given two tiles or more
+
+// The thread's four load addresses of one operand at k step k0 (all four advance by KT k
+// per step). KC = 1: rows tid / 8 + 32 c at k 4 (tid % 8); KC = 0: rows 4 (tid % 32) .. + 3
+// at k 4 (tid / 32) + c, c = 0 .. 3.
+template <int KC>
+__device__ __forceinline__ void big_ptrs(const float* X, int64_t sr, int64_t sk, int r0, int k0, const float*& p0,
+                                         const float*& p1, const float*& p2, const float*& p3) {
+  const int tid = threadIdx.x;
+  if constexpr (KC) {
+    p0 = X + (int64_t)(r0 + (tid >> 3)) * sr + (int64_t)(k0 + 4 * (tid & 7)) * sk;
+    p1 = p0 + 32 * sr;
+    p2 = p0 + 64 * sr;
+    p3 = p0 + 96 * sr;
+  } else {
+    p0 = X + (int64_t)(r0 + 4 * (tid & 31)) * sr + (int64_t)(k0 + 4 * (tid >> 5)) * sk;
+    p1 = p0 + sk;
+    p2 = p1 + sk;
+    p3 = p2 + sk;
+  }
+}
+
+// The four loaded float4 of one operand into the k-contiguous LDS tile.
+template <int KC>
+__device__ __forceinline__ void big_store(float* tile, float4 v0, float4 v1, float4 v2, float4 v3) {
+  const int tid = threadIdx.x;
+  if constexpr (KC) {
+    const int r = tid >> 3, k = 4 * (tid & 7);
+    *reinterpret_cast<float4*>(tile + (r + 0) * LDT + lds_col(r + 0, k)) = v0;
+    *reinterpret_cast<float4*>(tile + (r + 32) * LDT + lds_col(r + 32, k)) = v1;
+    *reinterpret_cast<float4*>(tile + (r + 64) * LDT + lds_col(r + 64, k)) = v2;
+    *reinterpret_cast<float4*>(tile + (r + 96) * LDT + lds_col(r + 96, k)) = v3;
+  } else {
+    const int r = 4 * (tid & 31), k = 4 * (tid >> 5);
+    *reinterpret_cast<float4*>(tile + (r + 0) * LDT + lds_col(r + 0, k)) = make_float4(v0.x, v1.x, v2.x, v3.x);
+    *reinterpret_cast<float4*>(tile + (r + 1) * LDT + lds_col(r + 1, k)) = make_float4(v0.y, v1.y, v2.y, v3.y);
+    *reinterpret_cast<float4*>(tile + (r + 2) * LDT + lds_col(r + 2, k)) = make_float4(v0.z, v1.z, v2.z, v3.z);
+    *reinterpret_cast<float4*>(tile + (r + 3) * LDT + lds_col(r + 3, k)) = make_float4(v0.w, v1.w, v2.w, v3.w);
+  }
+}
+
+// One 128 x 128 tile of C = alpha A B over k in [kbeg, kend), (kend - kbeg) a multiple of
+// KT. Per k step: one barrier (step s in LDS, step s - 1 retired), the next step's loads
+// issued into registers, this step's MFMAs, then the registers stored into the other buffer.
+template <int AKC, int BKC>
+__device__ __forceinline__ void gemm_tile_big(const GemmDesc& d, const float* A, const float* Bm, float* C, int m0, int n0,
+                                              int kbeg, int kend, float (*sA)[BMB * LDT], float (*sB)[BMB * LDT]) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float *pa0, *pa1, *pa2, *pa3, *pb0, *pb1, *pb2, *pb3;
+  big_ptrs<AKC>(A, d.am, d.ak, m0, kbeg, pa0, pa1, pa2, pa3);
+  big_ptrs<BKC>(Bm, d.bn, d.bk, n0, kbeg, pb0, pb1, pb2, pb3);
+  const int64_t sa = (int64_t)KT * d.ak, sb = (int64_t)KT * d.bk;
+  float4 a0, a1, a2, a3, b0, b1, b2, b3;
+  auto load = [&]() {
+    a0 = *reinterpret_cast<const float4*>(pa0);
+    a1 = *reinterpret_cast<const float4*>(pa1);
+    a2 = *reinterpret_cast<const float4*>(pa2);
+    a3 = *reinterpret_cast<const float4*>(pa3);
+    b0 = *reinterpret_cast<const float4*>(pb0);
+    b1 = *reinterpret_cast<const float4*>(pb1);
+    b2 = *reinterpret_cast<const float4*>(pb2);
+    b3 = *reinterpret_cast<const float4*>(pb3);
+    pa0 += sa; pa1 += sa; pa2 += sa; pa3 += sa;
+    pb0 += sb; pb1 += sb; pb2 += sb; pb3 += sb;
+  };
+  auto store = [&](int buf) {
+    big_store<AKC>(sA[buf], a0, a1, a2, a3);
+    big_store<BKC>(sB[buf], b0, b1, b2, b3);
+  };
+  auto step_mma = [&](int buf) {
+    const float* a_t = sA[buf];
+    const float* b_t = sB[buf];
+    f32x8 b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn + 16 * j + lc;
+      b[j] = load8<float>(b_t + r * LDT + lds_col(r, 8 * lg));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 16 * i + lc;
+      const f32x8 a = load8<float>(a_t + r * LDT + lds_col(r, 8 * lg));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(acc[i][j], a, b[j]);
+    }
+  };
+  const int nk = (kend - kbeg) / KT;
+  if (nk > 0) {
+    load();
+    store(0);
+  }
+  //   s_waitcnt lgkmcnt(0) before each barrier: this wave's LDS stores have landed before
+  //   the barrier publishes them. The scheduling barriers keep the loads ahead of the
+  //   MFMAs and the LDS stores (which wait for the loads) behind them.
+  auto body = [&](auto buf_c, int s) {
+    constexpr int buf = decltype(buf_c)::value;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();
+    const bool more = s + 1 < nk;
+    if (more) load();
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) store(buf ^ 1);
+  };
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    body(std::integral_constant<int, 0>{}, s);
+    body(std::integral_constant<int, 1>{}, s + 1);
+  }
+  if (s < nk) body(std::integral_constant<int, 0>{}, s);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * lg + r, n = n0 + wn + 16 * j + lc;
+        C[(int64_t)m * d.ldc + n] = d.alpha * acc[i][j][r];
+      }
+}
+
+// Tiles of up to three GEMMs that all satisfy big_tiles_ok, ordered as in gemm_f32_kernel.
+__global__ __launch_bounds__(256, 2) void gemm_f32_big_kernel(GemmDesc d0, GemmDesc d1, GemmDesc d2, int t0, int t1) {
+  __shared__ __attribute__((aligned(32))) float sA[2][BMB * LDT];
+  __shared__ __attribute__((aligned(32))) float sB[2][BMB * LDT];
+  const int bid = blockIdx.x;
+  const int which = bid < t0 ? 0 : (bid < t0 + t1 ? 1 : 2);
+  const GemmDesc& d = which == 0 ? d0 : (which == 1 ? d1 : d2);
+  const int ntn = d.N / BMB, tiles_mn = (d.M / BMB) * ntn;
+  const int t = bid - (which == 0 ? 0 : (which == 1 ? t0 : t0 + t1));
+  const int bi = t / (tiles_mn * d.nsplit), t2 = t % (tiles_mn * d.nsplit);
+  const int split = t2 / tiles_mn, tile = t2 % tiles_mn;
+  const int m0 = (tile / ntn) * BMB, n0 = (tile % ntn) * BMB;
+  const int kbeg = split * d.kchunk, kend = min(d.K, kbeg + d.kchunk);
+  const float* const A = d.A + bi * d.a_b;
+  const float* const Bm = d.B + bi * d.b_b;
+  float* const C = d.C + split * d.c_split + bi * d.c_b;
+  const int kc = d.a_kc * 2 + d.b_kc;
+  if (kc == 3) gemm_tile_big<1, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+  else if (kc == 2) gemm_tile_big<1, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+  else if (kc == 1) gemm_tile_big<0, 1>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+  else gemm_tile_big<0, 0>(d, A, Bm, C, m0, n0, kbeg, kend, sA, sB);
+}
+
+bool big_tiles_ok(const GemmDesc& d) {
+  return d.vec && d.tri == TRI_NONE && d.M % BMB == 0 && d.N % BMB == 0 && d.K % KT == 0 && d.kchunk % KT == 0 &&
+         d.kchunk > 0;
+}
+int tiles_big(const GemmDesc& d) { return (d.M / BMB) * (d.N / BMB) * d.nsplit * d.batch; }
+
+// One launch of the dX and dW products of a linear backward (either may be null).
+void launch_linear_pair(const GemmDesc* gx, const GemmDesc* gw, hipStream_t s) {
+  const bool big = (!gx || big_tiles_ok(*gx)) && (!gw || big_tiles_ok(*gw)) &&
+                   (gx ? tiles_big(*gx) : 0) + (gw ? tiles_big(*gw) : 0) >= kBigMinTiles;
+  const GemmDesc& a = gx ? *gx : *gw;
+  const GemmDesc& b = gw ? *gw : *gx;
+  if (big) {
+    const int ta = tiles_big(a), tb = gx && gw ? tiles_big(b) : 0;
+    hipLaunchKernelGGL(gemm_f32_big_kernel, dim3(ta + tb), dim3(256), 0, s, a, b, b, ta, tb);
+  } else {
+    const int ta = tiles_of(a), tb = gx && gw ? tiles_of(b) : 0;
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(ta + tb), dim3(256), 0, s, a, b, b, ta, tb);
+  }
+}
+
 // out[i] = sum over s of part[s * stride4 + i], in order s = 0, 1, ... (four elements per
 // lane; stride4 >= n4 in float4 units)
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restrict__ part, int ns, int64_t n4,
@@ -352,13 +537,8 @@ hipError_t launch_linear_bwd(const float* x, const float* w, const float* dy, fl
   if (T < 1 || K < 1 || N < 1) return hipErrorInvalidValue;
   GemmDesc gx, gw;
   linear_descs(x, w, dy, dx, dw, T, K, N, gx, gw);
-  const int tx = dx ? tiles_of(gx) : 0;
-  const int tw = dw ? tiles_of(gw) : 0;
-  if (tx + tw == 0) return hipSuccess;
-  if (tx)
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
-  else
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tw), dim3(256), 0, s, gw, gw, gw, tw, 0);
+  if (!dx && !dw) return hipSuccess;
+  launch_linear_pair(dx ? &gx : nullptr, dw ? &gw : nullptr, s);
   return hipGetLastError();
 }
 
@@ -386,8 +566,7 @@ hipError_t launch_linear_bwd_split(const float* x, const float* w, const float* 
   gx.nsplit = ns;
   gx.kchunk = ((nk + ns - 1) / ns) * KT;
   gx.c_split = (int64_t)T * K;
-  const int tx = tiles_of(gx), tw = tiles_of(gw);
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
+  launch_linear_pair(&gx, &gw, s);
   const int64_t n4 = (int64_t)T * K / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(part), ns, n4,
@@ -409,8 +588,7 @@ hipError_t launch_linear_bwd_parts(const float* x, const float* w, const float* 
   gx.nsplit = ns;
   gx.kchunk = ((nk + ns - 1) / ns) * KT;
   gx.c_split = (int64_t)T * K;
-  const int tx = tiles_of(gx), tw = tiles_of(gw);
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3(tx + tw), dim3(256), 0, s, gx, gw, gw, tx, tw);
+  launch_linear_pair(&gx, &gw, s);
   *ns_out = ns;
   return hipGetLastError();
 }
