@@ -124,9 +124,10 @@ int attn_bwd_noalloc(const attn_bwd_desc* desc, const void* q, const void* k, co
                      const void* dout, const float* lse, const float* P, void* dq, void* dk, void* dv,
                      vtb_stream_t stream);
 
-/* attn_bwd with per-kernel timing, for measurement: identical work and results. Every
- * call runs two kernels on `stream` (flash and MFMA paths: the query-parallel dq pass,
- * then the key-parallel dk/dv pass; decode path: the chunk pass, then the gradient pass;
+/* attn_bwd with per-kernel timing, for measurement: identical results. Every call runs
+ * two kernels on `stream` (flash and MFMA paths: the query-parallel dq pass, then the
+ * key-parallel dk/dv pass; decode path: the chunk pass, then the gradient pass, also when
+ * the keys fit one 64-key chunk, where attn_bwd runs one fused kernel instead;
  * Tq == 0: the zero fills of dk and dv), and the caller's HIP events (hipEvent_t,
  * created by the caller) are recorded by the dispatches themselves: events[0] and
  * events[1] at the start and end of the first kernel, events[2] and events[3] at the

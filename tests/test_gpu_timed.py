@@ -1,6 +1,7 @@
 """attn_bwd_timed (through the binding's events argument) against attn_bwd on the GPU: the
 same outputs bit for bit, and the four caller events recorded by the two kernels in order,
-on the MFMA path (bf16, d 128, lse given), the flash path (fp32, d 64) and the decode path."""
+on the MFMA path (bf16, d 128, lse given), the flash path (fp32, d 64) and the decode path
+(also with keys in one chunk, where the untimed call runs one fused kernel)."""
 
 import ctypes
 import os
@@ -46,6 +47,9 @@ CASES = [
     ("mfma_bf16_causal_d128", 2, 192, 192, 4, 2, 128, "bf16", True, True),
     ("flash_f32_causal_d64", 1, 100, 100, 3, 3, 64, "f32", True, False),
     ("decode_f32_gqa4", 2, 1, 300, 8, 2, 128, "f32", False, False),
+    # keys in one 64-key chunk: attn_bwd runs one fused kernel, the timed call its two kernels
+    ("decode_one_chunk_f32", 2, 1, 64, 8, 2, 128, "f32", False, False),
+    ("decode_one_chunk_bf16_causal_lse", 1, 3, 17, 4, 2, 64, "bf16", True, True),
 ]
 
 
