@@ -50,6 +50,8 @@ CASES = [
     # keys in one 64-key chunk: attn_bwd runs one fused kernel, the timed call its two kernels
     ("decode_one_chunk_f32", 2, 1, 64, 8, 2, 128, "f32", False, False),
     ("decode_one_chunk_bf16_causal_lse", 1, 3, 17, 4, 2, 64, "bf16", True, True),
+    ("decode_one_chunk_16_rows", 1, 1, 40, 16, 1, 128, "f32", False, False),
+    ("decode_one_key", 3, 2, 1, 6, 3, 64, "f32", False, False),
 ]
 
 
