@@ -37,7 +37,7 @@ typedef void* vtb_stream_t; /* a hipStream_t */
 typedef enum {
   VTB_OK = 0,
   VTB_ERR_ARG = 1,          /* bad shape, stride, NULL pointer or value */
-  VTB_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. head_dim 96) */
+  VTB_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement (e.g. head_dim 96) */
   VTB_ERR_ALIAS = 3,        /* an output overlaps an input or another output */
   VTB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the size query returns */
   VTB_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
