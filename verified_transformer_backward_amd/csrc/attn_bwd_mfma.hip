@@ -585,20 +585,34 @@ void fwd_mfma_kernel(AttnParams p) {
       const float mn = fmaxf(mrun[qt], bm);
       const float mref = mn == -INFINITY ? 0.f : mn;           // no visible key yet: every term is 0
       const float a = __builtin_amdgcn_exp2f(mrun[qt] - mref);  // 0 while the maximum is -inf
-      lrun[qt] *= a;
-      lrnd[qt] *= a;
+      // Rescale only when some query of the wave has a new maximum (a = 1 exactly
+      // otherwise, so skipping the products changes nothing).
+      if (__builtin_amdgcn_ballot_w64(a != 1.f)) {
+        lrun[qt] *= a;
+        lrnd[qt] *= a;
 #pragma unroll
-      for (int dt = 0; dt < kNDT; ++dt) acO[dt][qt] *= a;
+        for (int dt = 0; dt < kNDT; ++dt) acO[dt][qt] *= a;
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float e = __builtin_amdgcn_exp2f(s2[kt][qt][r] - mref);
-          const __bf16 eb = (__bf16)e;
           lrun[qt] += e;
-          lrnd[qt] += (float)eb;
-          pb[kt >> 1][qt][4 * (kt & 1) + r] = eb;
+          pb[kt >> 1][qt][4 * (kt & 1) + r] = (__bf16)e;
         }
+      // the sum of the bf16-rounded weights, two per instruction (each pair dotted with (1, 1))
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+      float t = lrnd[qt];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 p8 = pb[c][qt];
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), one2, t, false);
+      }
+      lrnd[qt] = t;
       mrun[qt] = mn;
     }
     fence();
