@@ -33,6 +33,8 @@ CASES = [
     ("bf16_mfma", (2, 256, 256, 4, 2, 128), (1, 130, 130, 2, 1, 128), "bf16", True, True),
     ("f32_flash", (1, 96, 120, 4, 2, 64), (1, 33, 40, 2, 2, 64), "f32", True, False),
     ("f32_decode", (4, 1, 700, 8, 2, 128), (2, 1, 300, 4, 1, 128), "f32", False, False),
+    # keys in one chunk: the fused one-launch decode path
+    ("f32_decode_one_chunk", (2, 1, 64, 8, 2, 128), (1, 1, 20, 4, 1, 64), "f32", False, False),
 ]
 
 
