@@ -279,7 +279,8 @@ def test_graph_replay_matches_eager():
 
 @pytest.mark.parametrize("case", [("bf16_mfma", 2, 192, 192, 4, 2, 128, "bf16", True, True),
                                   ("f32_flash", 1, 70, 90, 4, 2, 64, "f32", True, False),
-                                  ("f32_decode", 2, 1, 300, 8, 2, 128, "f32", False, False)],
+                                  ("f32_decode", 2, 1, 300, 8, 2, 128, "f32", False, False),
+                                  ("f32_decode_one_chunk", 2, 1, 50, 8, 2, 128, "f32", False, False)],
                          ids=lambda c: c[0])
 def test_optional_dk_dv(case):
     """dk and dv are optional: a NULL one is not written and the others are bit-identical to
